@@ -1,0 +1,7 @@
+"""MI355X-native 8-bit block-wise optimizer step.
+
+The compute path is the HIP library libbitopt.so (hand-written gfx950 kernels
+behind a C ABI); `bit_optimizers_block_amd.bitopt` is its ctypes binding and
+`bit_optimizers_block_amd.optim` a thin optimizer wrapper over torch tensors.
+"""
+__all__ = ["bitopt", "optim", "workloads"]

@@ -1,0 +1,149 @@
+"""Pins of the oracle's block-wise codec and number-format rounding.
+
+Pages: "8-bit Optimizers via Block-wise Quantization" (abstract: a tensor is split
+into blocks quantized independently, one scale per block); "[XPU] Implemented 8bit
+optimizers in triton #1692" (test body: dequantize_blockwise(code, absmax, A,
+blocksize) multiplies the codebook entry by its block's absmax).
+
+Nearest code: the oracle scans all 256 entries (the definition).  It is pinned
+here against numpy.searchsorted plus one neighbour comparison, a different route
+to the same answer, on every codebook value and bin boundary (and thousands of
+fp32 ulps around each) and on random inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+
+def _nearest_by_search(q, x):
+    x = np.asarray(x, np.float32)
+    i = np.searchsorted(q, x, side="right") - 1
+    i = np.clip(i, 0, 254)
+    lo, hi = q[i], q[i + 1]
+    up = (hi - x) < (x - lo)  # fp32 distances; a tie goes to the lower index
+    return (i + up).astype(np.uint8)
+
+
+def _ulp_neighbourhood(centers, k):
+    c = np.asarray(centers, np.float32)
+    bits = c.view(np.int32).astype(np.int64)
+    out = []
+    for d in range(-k, k + 1):
+        b = bits + d
+        # step through fp32 values in value order on either side of zero
+        v = np.where(c >= 0, b, bits - d).astype(np.int32).view(np.float32)
+        out.append(v)
+    v = np.concatenate(out)
+    return v[np.isfinite(v)]
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_nearest_matches_search_around_boundaries(oref, signed):
+    q = oref.dynamic_map(signed)
+    mids = ((q[:-1].astype(np.float64) + q[1:]) / 2).astype(np.float32)
+    x = np.concatenate([_ulp_neighbourhood(q, 512), _ulp_neighbourhood(mids, 512),
+                        np.float32([0.0, -0.0, 1.0, -1.0, 1.5, -1.5, 1e-30, -1e-30])])
+    got = oref.nearest(q, x)
+    np.testing.assert_array_equal(got, _nearest_by_search(q, x))
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_nearest_matches_search_random(oref, signed):
+    q = oref.dynamic_map(signed)
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-1.05, 1.05, 400_000),
+                        np.sign(rng.standard_normal(100_000)) * 10.0 ** rng.uniform(-9, 0, 100_000)])
+    x = x.astype(np.float32)
+    np.testing.assert_array_equal(oref.nearest(q, x), _nearest_by_search(q, x))
+
+
+def test_nearest_exact_entries(oref):
+    for signed in (True, False):
+        q = oref.dynamic_map(signed)
+        np.testing.assert_array_equal(oref.nearest(q, q), np.arange(256, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("blocksize", [256, 2048])
+def test_quantize_recovers_codes_of_scaled_codebook(oref, blocksize):
+    """x = A_b * Q[k] with one k = 255 (value A_b) per block encodes back to k."""
+    q = oref.dynamic_map(True)
+    rng = np.random.default_rng(3)
+    nb = 9
+    n = nb * blocksize - 17
+    k = rng.integers(0, 256, n).astype(np.uint8)
+    A = (10.0 ** rng.uniform(-6, 1, nb)).astype(np.float32)
+    k[np.arange(nb) * blocksize] = 255
+    x = (q[k] * A[np.arange(n) // blocksize]).astype(np.float32)
+    codes, absmax = oref.quantize_blockwise(x, "f32", q, blocksize)
+    np.testing.assert_array_equal(absmax, A)
+    np.testing.assert_array_equal(codes, k)
+
+
+@pytest.mark.parametrize("n,blocksize", [(1, 256), (255, 256), (256, 256), (257, 256),
+                                         (2047, 2048), (2049, 2048), (100, 2048), (5000, 256)])
+def test_quantize_tail_and_error_bound(oref, n, blocksize):
+    qs = oref.dynamic_map(True)
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal(n) * 0.01).astype(np.float32)
+    codes, absmax = oref.quantize_blockwise(x, "f32", qs, blocksize)
+    nb = (n + blocksize - 1) // blocksize
+    assert absmax.shape == (nb,)
+    for b in range(nb):
+        blk = x[b * blocksize:(b + 1) * blocksize]
+        assert absmax[b] == np.abs(blk).max()          # exact, valid elements only
+    # dequantize is the codebook entry times the block scale
+    deq = oref.dequantize_blockwise(codes, absmax, qs, blocksize)
+    blk_a = absmax[np.arange(n) // blocksize]
+    np.testing.assert_array_equal(deq, (qs[codes] * blk_a).astype(np.float32))
+    # round-trip error: half the local codebook gap times the scale, plus rounding
+    qd = qs.astype(np.float64)
+    gaps = np.maximum(np.diff(qd, prepend=qd[0]), np.diff(qd, append=qd[-1]))
+    bound = blk_a.astype(np.float64) * (gaps[codes] / 2) * (1 + 1e-6) + np.abs(x) * 1e-6
+    assert np.all(np.abs(deq.astype(np.float64) - x) <= bound)
+    # a second pass over the decoded values changes nothing in blocks whose largest
+    # magnitude is positive (+1.0 is in the map, -1.0 is not)
+    codes2, absmax2 = oref.quantize_blockwise(deq, "f32", qs, blocksize)
+    assert np.all(absmax2 <= absmax)
+    for b in range(nb):
+        sl = slice(b * blocksize, min(n, (b + 1) * blocksize))
+        if x[sl][np.argmax(np.abs(x[sl]))] > 0:
+            assert absmax2[b] == absmax[b]
+            np.testing.assert_array_equal(codes2[sl], codes[sl])
+
+
+def test_quantize_zero_block(oref):
+    for signed, zero_code in ((True, 127), (False, 0)):
+        q = oref.dynamic_map(signed)
+        x = np.zeros(300, np.float32)
+        x[256:] = 0.5
+        codes, absmax = oref.quantize_blockwise(x, "f32", q, 256)
+        assert absmax[0] == 0.0 and np.all(codes[:256] == zero_code)
+        assert absmax[1] == 0.5 and np.all(codes[256:] == 255)
+
+
+def test_fp16_rounding_matches_numpy(oref):
+    rng = np.random.default_rng(11)
+    specials = np.float32([0.0, -0.0, 65504.0, 65519.996, 65520.0, 1e6, -1e6, 6.0e-8, 2.98e-8,
+                           2.9802322e-08, 5.9604645e-08, 6.1035156e-05, 6.103515e-05, np.inf, -np.inf,
+                           1.0009765625, 1.00048828125, 1.000732421875, 2049.0, 2051.0])
+    x = np.concatenate([specials, (rng.standard_normal(200_000) * 10.0 ** rng.uniform(-9, 5, 200_000))
+                        .astype(np.float32), rng.integers(0, 2 ** 32, 200_000, dtype=np.uint64)
+                        .astype(np.uint32).view(np.float32)])
+    x = x[~np.isnan(x)]
+    got = oref.round_to_dtype(x, "f16")
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16)
+    np.testing.assert_array_equal(got.view(np.uint16), ref.view(np.uint16))
+    np.testing.assert_array_equal(oref.widen(got, "f16"), got.astype(np.float32))
+
+
+def test_bf16_rounding_matches_torch(oref):
+    rng = np.random.default_rng(12)
+    x = np.concatenate([np.float32([0.0, -0.0, 1.00390625, 1.01171875, 3.3895314e38, np.inf]),
+                        rng.integers(0, 2 ** 32, 300_000, dtype=np.uint64).astype(np.uint32).view(np.float32)])
+    x = x[~np.isnan(x)]
+    got = oref.round_to_dtype(x, "bf16")
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(oref.widen(got, "bf16"),
+                                  torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy())

@@ -1,0 +1,532 @@
+"""Pins of the oracle's optimizer updates.
+
+Pages:
+  "optim_overview" (Optimizer2State / Optimizer1State hyper-parameters: lr, betas,
+    eps, weight_decay, max_unorm, skip_zeros, alpha, t_alpha, t_beta3);
+  "[XPU] Implemented 8bit optimizers in triton #1692" (optimizer table: the 8-bit
+    optimizers are checked against torch.optim.Adam / AdamW / SGD(p, 0.01, 0.9), a
+    Lion implementation and a reference AdEMAMix; test body: 50-step tracking
+    protocol with re-sync and its tolerances);
+  "Support skip_zeros in the XPU Triton optimizer kernels #2097" (description and
+    Tests: zero-gradient elements untouched, the rest identical to skip_zeros=False;
+    zero test on the raw gradient; default path unchanged).
+
+What pins what:
+  * 32-bit mode (identity codec) vs torch.optim.AdamW / SGD run in float64, and vs
+    float64 statements of Lion and AdEMAMix written in their papers' form (bias-
+    corrected moments, decoupled decay term inside the step), over 10 steps.
+  * Closed forms at t = 1 from a zero state.
+  * AdEMAMix with alpha = 0 is bit-identical to Adam (the extra slow EMA drops out).
+  * AdEMAMix schedules: endpoints and the linear-in-t half-life of beta3(t).
+  * 8-bit mode tracks the 32-bit optimizers under the pages' re-sync protocol and
+    tolerances (tests/golden/p1_tracking_tolerances.json).
+  * skip_zeros and max_unorm invariants; thread-count independence.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from bit_optimizers_block_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+f32 = np.float32
+
+
+def _close(a, b, rtol=1e-5):
+    """fp32-vs-fp64 agreement: relative, with an absolute floor of rtol/10 of the array's
+    scale (EMA states pass through zero, where relative error means nothing)."""
+    b = np.asarray(b, np.float64)
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=rtol * 0.1 * np.abs(b).max())
+
+
+def _f(x):
+    """The fp32 value of a hyper-parameter, as a Python float (what both sides use)."""
+    return float(np.float32(x))
+
+
+def _inputs(n, steps, seed, p_scale=0.02, g_scale=0.01, dtype="f32"):
+    p = W.to_dtype(W.normal_f32([seed, 1], n, p_scale), dtype)
+    gs = [W.to_dtype(W.normal_f32([seed, 2, t], n, g_scale), dtype) for t in range(1, steps + 1)]
+    return p, gs
+
+
+def _run32(oref, hp, p, gs, dtype="f32"):
+    n = p.size
+    ns = oref.NUM_STATES[hp["optimizer"]]
+    s1 = np.zeros(2 * n if hp["optimizer"] == "ademamix" else n, f32)
+    s2 = np.zeros(n, f32) if ns >= 2 else None
+    p = p.copy()
+    for t, g in enumerate(gs, 1):
+        oref.step_32bit(hp, t, p, g, dtype, s1, s2)
+    return p, s1, s2
+
+
+def _new8(oref, hp, n):
+    B = hp.get("blocksize", 256)
+    nb = (n + B - 1) // B
+    opt = hp["optimizer"]
+    st = dict(state1=np.zeros(2 * n if opt == "ademamix" else n, np.uint8),
+              absmax1=np.zeros(2 * nb if opt == "ademamix" else nb, f32),
+              qmap1=oref.dynamic_map(True))
+    if oref.NUM_STATES[opt] >= 2:
+        st.update(state2=np.zeros(n, np.uint8), absmax2=np.zeros(nb, f32), qmap2=oref.dynamic_map(False))
+    return st
+
+
+def _step8(oref, hp, t, p, g, dtype, st, blocks=None):
+    oref.step_8bit(hp, t, p, g, dtype, st["state1"], st["absmax1"], st["qmap1"],
+                   st.get("state2"), st.get("absmax2"), st.get("qmap2"), blocks=blocks)
+
+
+# ----------------------------------------------------------------------------- 32-bit vs fp64
+
+def _torch64(opt_ctor, p0, gs):
+    p = torch.nn.Parameter(torch.from_numpy(p0.astype(np.float64)))
+    opt = opt_ctor([p])
+    for g in gs:
+        p.grad = torch.from_numpy(g.astype(np.float64))
+        opt.step()
+    return p.detach().numpy(), opt.state[p]
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.01])
+def test_adam_32bit_matches_torch_adamw_fp64(oref, wd):
+    p0, gs = _inputs(3000, 10, 21)
+    hp = dict(optimizer="adam", lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd)
+    p, m, v = _run32(oref, hp, p0, gs)
+    ref_p, st = _torch64(lambda ps: torch.optim.AdamW(ps, lr=_f(1e-3), betas=(_f(0.9), _f(0.999)),
+                                                        eps=_f(1e-8), weight_decay=_f(wd), foreach=False),
+                         p0, gs)
+    np.testing.assert_allclose(p, ref_p, rtol=1e-6, atol=1e-8)
+    _close(m, st["exp_avg"].numpy())
+    _close(v, st["exp_avg_sq"].numpy())
+
+
+def test_momentum_32bit_matches_torch_sgd_fp64(oref):
+    p0, gs = _inputs(3000, 10, 22)
+    hp = dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01)
+    p, buf, _ = _run32(oref, hp, p0, gs)
+    ref_p, st = _torch64(lambda ps: torch.optim.SGD(ps, lr=_f(0.01), momentum=_f(0.9),
+                                                      weight_decay=_f(0.01), foreach=False), p0, gs)
+    np.testing.assert_allclose(p, ref_p, rtol=1e-6, atol=1e-8)
+    _close(buf, st["momentum_buffer"].numpy())
+
+
+def _lion64(p0, gs, lr, b1, b2, wd):
+    """Lion as its paper states it: update = sign(b1*m + (1-b1)*g);
+    p <- p - lr*(update + wd*p); m <- b2*m + (1-b2)*g."""
+    p = p0.astype(np.float64)
+    m = np.zeros_like(p)
+    for g in gs:
+        g = g.astype(np.float64)
+        upd = np.sign(b1 * m + (1 - b1) * g)
+        p = p - lr * (upd + wd * p)
+        m = b2 * m + (1 - b2) * g
+    return p, m
+
+
+def test_lion_32bit_matches_fp64(oref):
+    p0, gs = _inputs(3000, 10, 23)
+    hp = dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01)
+    p, m, _ = _run32(oref, hp, p0, gs)
+    ref_p, ref_m = _lion64(p0, gs, _f(1e-4), _f(0.9), _f(0.99), _f(0.01))
+    np.testing.assert_allclose(p, ref_p, rtol=1e-6, atol=1e-9)
+    _close(m, ref_m)
+
+
+def _ademamix64(p0, gs, lr, b1, b2, b3, alpha, eps, wd, t_alpha, t_beta3):
+    """AdEMAMix in its paper's form: fast EMA m1 (bias-corrected), slow EMA m2 (not
+    bias-corrected) mixed with weight alpha, second moment nu (bias-corrected),
+    decoupled weight decay inside the step; alpha and beta3 warm up over t_alpha and
+    t_beta3 steps (beta3's half-life grows linearly from beta1's)."""
+    p = p0.astype(np.float64)
+    m1 = np.zeros_like(p); m2 = np.zeros_like(p); nu = np.zeros_like(p)
+    for t, g in enumerate(gs, 1):
+        g = g.astype(np.float64)
+        a = alpha * min(t / t_alpha, 1.0) if t_alpha else alpha
+        if t_beta3:
+            h1, h3 = np.log(0.5) / np.log(b1), np.log(0.5) / np.log(b3)
+            h = (1 - t / t_beta3) * h1 + (t / t_beta3) * h3     # half-life, linear in t
+            bt = min(0.5 ** (1.0 / h), b3)
+        else:
+            bt = b3
+        m1 = b1 * m1 + (1 - b1) * g
+        m2 = bt * m2 + (1 - bt) * g
+        nu = b2 * nu + (1 - b2) * g * g
+        m1h = m1 / (1 - b1 ** t)
+        nuh = nu / (1 - b2 ** t)
+        p = p - lr * ((m1h + a * m2) / (np.sqrt(nuh) + eps) + wd * p)
+    return p, m1, m2, nu
+
+
+@pytest.mark.parametrize("sched", [None, 5])
+def test_ademamix_32bit_matches_fp64(oref, sched):
+    p0, gs = _inputs(3000, 10, 24)
+    hp = dict(optimizer="ademamix", lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0,
+              eps=1e-8, weight_decay=0.01, t_alpha=sched, t_beta3=sched)
+    p, m12, nu = _run32(oref, hp, p0, gs)
+    ref = _ademamix64(p0, gs, _f(1e-3), _f(0.9), _f(0.999), _f(0.9999), 5.0, _f(1e-8), _f(0.01),
+                      sched, sched)
+    np.testing.assert_allclose(p, ref[0], rtol=1e-6, atol=1e-8)
+    _close(m12[:3000], ref[1])
+    _close(m12[3000:], ref[2])
+    _close(nu, ref[3])
+
+
+def test_ademamix_schedules(oref):
+    b1, b3, T = _f(0.9), _f(0.9999), 100
+    assert oref.beta3_schedule(b1, b3, 0, T) == pytest.approx(b1, rel=1e-12)
+    assert oref.beta3_schedule(b1, b3, T, T) == pytest.approx(b3, rel=1e-12)
+    assert oref.beta3_schedule(b1, b3, 3 * T, T) == b3             # capped at beta3
+    assert oref.beta3_schedule(b1, b3, 7, 0) == b3                 # no schedule
+    # the slow EMA's half-life grows linearly in t
+    ts = np.arange(0, T + 1)
+    hl = np.array([np.log(0.5) / np.log(oref.beta3_schedule(b1, b3, int(t), T)) for t in ts])
+    np.testing.assert_allclose(np.diff(hl, 2), 0.0, atol=1e-6 * hl.max())
+    assert np.all(np.diff(hl) > 0)
+    assert oref.alpha_schedule(5.0, 1, T) == pytest.approx(0.05)
+    assert oref.alpha_schedule(5.0, 50, T) == pytest.approx(2.5)
+    assert oref.alpha_schedule(5.0, 100, T) == 5.0 and oref.alpha_schedule(5.0, 250, T) == 5.0
+    assert oref.alpha_schedule(5.0, 3, None) == 5.0
+
+
+# ----------------------------------------------------------------------------- closed forms at t = 1
+
+def test_first_step_closed_forms(oref):
+    n = 1000
+    rng = np.random.default_rng(5)
+    p0 = (rng.standard_normal(n) * 0.02).astype(f32)
+    g = (np.sign(rng.standard_normal(n)) * 1e-2).astype(f32)
+    for mode in ("32", "8"):
+        # Adam: at t = 1 the bias-corrected moments are g and g^2: step = lr*g/(|g|+eps)
+        hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01)
+        p = p0.copy()
+        if mode == "32":
+            oref.step_32bit(hp, 1, p, g, "f32", np.zeros(n, f32), np.zeros(n, f32))
+        else:
+            _step8(oref, hp, 1, p, g, "f32", _new8(oref, hp, n))
+        expect = p0 * (1 - 1e-3 * 0.01) - 1e-3 * g / (np.abs(g) + 1e-8)
+        np.testing.assert_allclose(p, expect, rtol=2e-6, atol=1e-9)
+        assert np.allclose((p - p0 * f32(1 - 1e-5))[g > 0], -9.99999e-4, rtol=1e-5)
+        # Momentum: the buffer starts as the decayed gradient
+        hp = dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01)
+        p = p0.copy()
+        if mode == "32":
+            oref.step_32bit(hp, 1, p, g, "f32", np.zeros(n, f32))
+        else:
+            _step8(oref, hp, 1, p, g, "f32", _new8(oref, hp, n))
+        np.testing.assert_allclose(p, p0 - 0.01 * (g + 0.01 * p0), rtol=1e-6, atol=1e-10)
+        # Lion: p' = p*(1 - lr*wd) - lr*sign(g)
+        hp = dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01)
+        p = p0.copy()
+        if mode == "32":
+            oref.step_32bit(hp, 1, p, g, "f32", np.zeros(n, f32))
+        else:
+            _step8(oref, hp, 1, p, g, "f32", _new8(oref, hp, n))
+        np.testing.assert_allclose(p, p0 * (1 - 1e-6) - 1e-4 * np.sign(g), rtol=1e-6, atol=1e-10)
+        # AdEMAMix: u = (g + alpha(1)*(1-beta3(1))*g)/(|g| + eps)
+        hp = dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0, t_alpha=100, t_beta3=100)
+        p = p0.copy()
+        if mode == "32":
+            oref.step_32bit(hp, 1, p, g, "f32", np.zeros(2 * n, f32), np.zeros(n, f32))
+        else:
+            _step8(oref, hp, 1, p, g, "f32", _new8(oref, hp, n))
+        b3 = oref.beta3_schedule(_f(0.9), _f(0.9999), 1, 100)
+        expect = p0 - 1e-3 * (g + 0.05 * (1 - b3) * g) / (np.abs(g) + 1e-8)
+        np.testing.assert_allclose(p, expect, rtol=2e-6, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------- AdEMAMix(alpha=0) == Adam
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ademamix_alpha0_is_adam_bitwise(oref, dtype):
+    n, steps = 5000, 6
+    p0, gs = _inputs(n, steps, 25, dtype=dtype)
+    ha = dict(optimizer="adam", lr=1e-3, weight_decay=0.01)
+    he = dict(optimizer="ademamix", lr=1e-3, weight_decay=0.01, alpha=0.0, beta3=0.9999)
+    pa, pe = p0.copy(), p0.copy()
+    sa, se = _new8(oref, ha, n), _new8(oref, he, n)
+    for t, g in enumerate(gs, 1):
+        _step8(oref, ha, t, pa, g, dtype, sa)
+        _step8(oref, he, t, pe, g, dtype, se)
+    np.testing.assert_array_equal(pa, pe)
+    np.testing.assert_array_equal(sa["state1"], se["state1"][:n])
+    np.testing.assert_array_equal(sa["state2"], se["state2"])
+    nb = sa["absmax1"].size
+    np.testing.assert_array_equal(sa["absmax1"], se["absmax1"][:nb])
+    np.testing.assert_array_equal(sa["absmax2"], se["absmax2"])
+
+
+# ----------------------------------------------------------------------------- 8-bit tracks 32-bit
+
+def _ref32_torch(name):
+    if name == "adam":
+        return lambda ps: torch.optim.Adam(ps, lr=_f(1e-3), betas=(_f(0.9), _f(0.999)), eps=_f(1e-8))
+    if name == "momentum":
+        return lambda ps: torch.optim.SGD(ps, lr=_f(0.01), momentum=_f(0.9))
+    return None
+
+
+class _Ref32:
+    """fp32 comparator holding named states, stepped one step at a time."""
+
+    def __init__(self, name, p):
+        self.name = name
+        self.p = torch.nn.Parameter(torch.from_numpy(p.copy()))
+        ctor = _ref32_torch(name)
+        self.opt = ctor([self.p]) if ctor else None
+        self.t = 0
+        n = p.size
+        if name == "lion":
+            self.m = torch.zeros(n)
+        if name == "ademamix":
+            self.m1 = torch.zeros(n); self.m2 = torch.zeros(n); self.nu = torch.zeros(n)
+
+    def step(self, g):
+        self.t += 1
+        g = torch.from_numpy(g.astype(np.float32))
+        with torch.no_grad():
+            if self.opt is not None:
+                self.p.grad = g
+                self.opt.step()
+            elif self.name == "lion":
+                b1, b2, lr = 0.9, 0.99, 1e-4
+                self.p -= lr * torch.sign(b1 * self.m + (1 - b1) * g)
+                self.m.mul_(b2).add_((1 - b2) * g)
+            else:  # ademamix, no schedule, alpha 5
+                b1, b2, b3, a, lr, eps = 0.9, 0.999, 0.9999, 5.0, 1e-3, 1e-8
+                self.m1.mul_(b1).add_((1 - b1) * g)
+                self.m2.mul_(b3).add_((1 - b3) * g)
+                self.nu.mul_(b2).add_((1 - b2) * g * g)
+                den = (self.nu / (1 - b2 ** self.t)).sqrt() + eps
+                self.p -= lr * (self.m1 / (1 - b1 ** self.t) + a * self.m2) / den
+
+    def states(self):
+        if self.name == "adam":
+            s = self.opt.state[self.p]
+            return [s["exp_avg"], s["exp_avg_sq"]]
+        if self.name == "momentum":
+            return [self.opt.state[self.p]["momentum_buffer"]]
+        if self.name == "lion":
+            return [self.m]
+        return [self.m1, self.m2, self.nu]
+
+    def set_states(self, vals):
+        for dst, v in zip(self.states(), vals):
+            dst.copy_(torch.from_numpy(v))
+
+
+@pytest.mark.parametrize("name,dtype", [("adam", "f32"), ("adam", "f16"), ("momentum", "f32"),
+                                        ("lion", "f32"), ("ademamix", "bf16")])
+def test_8bit_tracks_32bit_with_resync(oref, name, dtype):
+    tol = json.load(open(os.path.join(GOLDEN, "p1_tracking_tolerances.json")))
+    pt = tol["param"][dtype]
+    B = tol["blocksize"]
+    shape = (256, 256)
+    n = shape[0] * shape[1]
+    hp = {"adam": dict(optimizer="adam", lr=1e-3),
+          "momentum": dict(optimizer="momentum", lr=0.01, beta1=0.9),
+          "lion": dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99),
+          "ademamix": dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0)}[name]
+    hp["blocksize"] = B
+    steps = tol["steps"] if name == "adam" and dtype == "f32" else 20
+    p8 = W.to_dtype(W.normal_f32([77, 1], n, tol["param_scale"]), dtype)
+    p32 = oref.widen(p8, dtype) if dtype != "f32" else p8.copy()
+    ref = _Ref32(name, p32)
+    st = _new8(oref, hp, n)
+    nb = n // B
+    for t in range(1, steps + 1):
+        g = W.to_dtype(W.normal_f32([77, 2, t], n, tol["gradient_scale"]), dtype)
+        ref.step(oref.widen(g, dtype) if dtype != "f32" else g)
+        _step8(oref, hp, t, p8, g, dtype, st)
+        a = ref.p.detach().numpy()
+        b = oref.widen(p8, dtype) if dtype != "f32" else p8
+        not_close = ~np.isclose(a, b, rtol=pt["prtol"], atol=pt["patol"])
+        assert not_close.sum() <= pt["max_error_count"], (t, not_close.sum())
+        # decoded 8-bit states against the 32-bit comparator's states
+        deq = []
+        for k, rs in enumerate(ref.states()):
+            if name == "ademamix" and k < 2:
+                codes, am, q = st["state1"][k * n:(k + 1) * n], st["absmax1"][k * nb:(k + 1) * nb], st["qmap1"]
+            elif k == 0:
+                codes, am, q = st["state1"], st["absmax1"], st["qmap1"]
+            else:
+                codes, am, q = st["state2"], st["absmax2"], st["qmap2"]
+            d = oref.dequantize_blockwise(codes, am, q, B)
+            nc = ~np.isclose(rs.numpy(), d, atol=tol["state_atol"], rtol=tol["state_rtol"])
+            assert nc.sum() < tol["state_max_not_close"]
+            deq.append(d)
+        err = np.abs(a - b)
+        rel = err / (np.abs(a) + 1e-9)
+        if dtype == "bf16":
+            assert err.mean() <= pt["mean_abs_le"] and rel.mean() <= pt["mean_rel_le"]
+        else:
+            assert err.mean() < pt["mean_abs_lt"] and rel.mean() < pt["mean_rel_lt"]
+        # re-sync the comparator to the 8-bit result (parameters and decoded states)
+        with torch.no_grad():
+            ref.p.copy_(torch.from_numpy(b.astype(np.float32)))
+        ref.set_states(deq)
+
+
+# ----------------------------------------------------------------------------- skip_zeros
+
+def _sparse_grad(n, B, seed, dtype):
+    rng = np.random.default_rng(seed)
+    g = (rng.standard_normal(n) * 0.01).astype(f32)
+    g[rng.random(n) < 0.3] = 0.0                       # scattered exact zeros
+    nb = (n + B - 1) // B
+    for b in rng.choice(nb, max(1, nb // 4), replace=False):
+        g[b * B:(b + 1) * B] = 0.0                     # whole zero blocks
+    g[5] = -0.0                                        # negative zero counts as zero
+    return W.to_dtype(g, dtype)
+
+
+OPT_HP = {
+    "adam": dict(optimizer="adam", lr=1e-3, weight_decay=0.01),
+    "ademamix": dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0, t_alpha=10, t_beta3=10,
+                     weight_decay=0.01),
+    "momentum": dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01),
+    "lion": dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01),
+}
+
+
+@pytest.mark.parametrize("name", list(OPT_HP))
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_skip_zeros_invariants_8bit(oref, name, dtype):
+    n, B = 256 * 40 + 77, 256
+    nb = (n + B - 1) // B
+    hp = dict(OPT_HP[name], blocksize=B)
+    # a non-trivial pre-step state: two dense steps first
+    p = W.to_dtype(W.normal_f32([31, 1], n, 0.02), dtype)
+    st = _new8(oref, hp, n)
+    for t in (1, 2):
+        _step8(oref, hp, t, p, W.to_dtype(W.normal_f32([31, 2, t], n, 0.01), dtype), dtype, st)
+    g = _sparse_grad(n, B, 32, dtype)
+    zero = oref.widen(g, dtype) == 0.0 if dtype != "f32" else g == 0.0
+
+    runs = {}
+    for key, extra in (("on", dict(skip_zeros=True)), ("off", dict(skip_zeros=False)), ("absent", {})):
+        h = {k: v for k, v in hp.items() if k != "skip_zeros"}
+        h.update(extra)
+        pp, ss = p.copy(), {k: v.copy() for k, v in st.items()}
+        _step8(oref, h, 3, pp, g, dtype, ss)
+        runs[key] = (pp, ss)
+    p_on, s_on = runs["on"]
+    p_off, s_off = runs["off"]
+    # zero-gradient elements keep their exact bits; the others match skip_zeros=False bit for bit
+    np.testing.assert_array_equal(p_on[zero], p[zero])
+    np.testing.assert_array_equal(p_on[~zero], p_off[~zero])
+    # skip_zeros=False is the default path (A/B against a call without the flag)
+    np.testing.assert_array_equal(p_off, runs["absent"][0])
+    for k in s_off:
+        np.testing.assert_array_equal(s_off[k], runs["absent"][1][k])
+    # blocks whose every gradient is zero: codes and absmax untouched
+    nstate = 2 if name == "ademamix" else 1
+    for b in range(nb):
+        sl = slice(b * B, min(n, (b + 1) * B))
+        if zero[sl].all():
+            for j in range(nstate):
+                off = j * n
+                np.testing.assert_array_equal(s_on["state1"][off + sl.start: off + sl.stop],
+                                              st["state1"][off + sl.start: off + sl.stop])
+                assert s_on["absmax1"][j * nb + b] == st["absmax1"][j * nb + b]
+            if "state2" in st:
+                np.testing.assert_array_equal(s_on["state2"][sl], st["state2"][sl])
+                assert s_on["absmax2"][b] == st["absmax2"][b]
+    # mixed blocks: a skipped element's decoded state stays within one local gap of its old value
+    q = st["qmap1"].astype(np.float64)
+    gap = np.maximum(np.diff(q, prepend=q[0]), np.diff(q, append=q[-1]))
+    old = oref.dequantize_blockwise(st["state1"][:n], st["absmax1"][:nb], st["qmap1"], B).astype(np.float64)
+    new = oref.dequantize_blockwise(s_on["state1"][:n], s_on["absmax1"][:nb], st["qmap1"], B)
+    amax = np.maximum(st["absmax1"][:nb], s_on["absmax1"][:nb])[np.arange(n) // B].astype(np.float64)
+    bound = amax * gap[s_on["state1"][:n]] * 1.01 + 1e-12
+    assert np.all(np.abs(new - old)[zero] <= bound[zero])
+
+
+@pytest.mark.parametrize("name", list(OPT_HP))
+def test_skip_zeros_32bit_states_untouched(oref, name):
+    n = 3000
+    hp = OPT_HP[name]
+    p = W.normal_f32([41, 1], n, 0.02)
+    s1 = W.normal_f32([41, 3], 2 * n if name == "ademamix" else n, 1e-3)
+    s2 = np.abs(W.normal_f32([41, 4], n, 1e-5)) if name in ("adam", "ademamix") else None
+    g = _sparse_grad(n, 256, 42, "f32")
+    zero = g == 0.0
+    pp, a1, a2 = p.copy(), s1.copy(), None if s2 is None else s2.copy()
+    oref.step_32bit(dict(hp, skip_zeros=True), 4, pp, g, "f32", a1, a2)
+    np.testing.assert_array_equal(pp[zero], p[zero])
+    np.testing.assert_array_equal(a1[:n][zero], s1[:n][zero])
+    if name == "ademamix":
+        np.testing.assert_array_equal(a1[n:][zero], s1[n:][zero])
+    if s2 is not None:
+        np.testing.assert_array_equal(a2[zero], s2[zero])
+    # with weight decay > 0 the zero test is still on the raw gradient: the decay
+    # term does not make a zero-gradient element move
+    assert hp["weight_decay"] > 0 and np.all(pp[zero] == p[zero])
+
+
+# ----------------------------------------------------------------------------- max_unorm
+
+@pytest.mark.parametrize("name", ["adam", "momentum", "lion", "ademamix"])
+def test_max_unorm(oref, name):
+    n, B = 256 * 12 + 5, 256
+    hp = dict(OPT_HP[name], blocksize=B, weight_decay=0.0)
+    p0 = W.normal_f32([51, 1], n, 0.02)
+    g = W.normal_f32([51, 2], n, 0.01)
+    outs = {}
+    for mu in (0.0, 1e30, 0.002):
+        p = p0.copy()
+        _step8(oref, dict(hp, max_unorm=mu), 1, p, g, "f32", _new8(oref, hp, n))
+        outs[mu] = p
+    np.testing.assert_array_equal(outs[0.0], outs[1e30])       # a limit never reached is no limit
+    assert not np.array_equal(outs[0.0], outs[0.002])
+    d_free = (p0 - outs[0.0]).astype(np.float64)
+    d_clip = (p0 - outs[0.002]).astype(np.float64)
+    for b in range((n + B - 1) // B):
+        sl = slice(b * B, (b + 1) * B)
+        un, pn = np.linalg.norm(d_clip[sl]), np.linalg.norm(p0[sl].astype(np.float64))
+        assert un <= 0.002 * pn * (1 + 1e-4) + 1e-9
+        if np.linalg.norm(d_free[sl]) > 0.002 * pn * (1 + 1e-4):
+            # clipped blocks keep the direction of the free update
+            c = np.dot(d_clip[sl], d_free[sl]) / (np.linalg.norm(d_free[sl]) * un)
+            assert c > 1 - 1e-6
+
+
+# ----------------------------------------------------------------------------- determinism
+
+def test_thread_count_independent(oref):
+    n = 256 * 300 + 9
+    hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01)
+    res = []
+    for th in (1, 4):
+        oref.set_threads(th)
+        p = W.normal_f32([61, 1], n, 0.02)
+        st = _new8(oref, hp, n)
+        for t in (1, 2, 3):
+            _step8(oref, hp, t, p, W.normal_f32([61, 2, t], n, 0.01), "f32", st)
+        res.append((p, st))
+    oref.set_threads(os.cpu_count() or 1)
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    for k in res[0][1]:
+        np.testing.assert_array_equal(res[0][1][k], res[1][1][k])
+
+
+def test_block_subset_equals_full_step(oref):
+    """The sampled-block mode computes exactly the listed blocks of a full step."""
+    n, B = 256 * 50 + 31, 256
+    hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01, blocksize=B)
+    p = W.normal_f32([71, 1], n, 0.02)
+    g = W.normal_f32([71, 2], n, 0.01)
+    full_p, full_s = p.copy(), _new8(oref, hp, n)
+    _step8(oref, hp, 1, full_p, g, "f32", full_s)
+    blocks = np.array([0, 7, 49, 50])
+    sub_p, sub_s = p.copy(), _new8(oref, hp, n)
+    _step8(oref, hp, 1, sub_p, g, "f32", sub_s, blocks=blocks)
+    for b in blocks:
+        sl = slice(b * B, min(n, (b + 1) * B))
+        np.testing.assert_array_equal(sub_p[sl], full_p[sl])
+        np.testing.assert_array_equal(sub_s["state1"][sl], full_s["state1"][sl])
+        assert sub_s["absmax2"][b] == full_s["absmax2"][b]
