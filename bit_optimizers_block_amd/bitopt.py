@@ -1,0 +1,222 @@
+"""ctypes binding of libbitopt.so (include/bitopt.h), argument marshalling only.
+
+Every function takes torch tensors (device tensors for device entry points),
+checks shapes/dtypes/devices, passes raw pointers and the current HIP stream to
+the C ABI, and raises BitoptError on a non-zero status.  All arithmetic of the
+step runs in the library's HIP kernels; if the library is not built, loading
+fails with an error instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitopt.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE = 0, -1, -2, -3
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+OPTIMIZERS = {"adam": 0, "adamw": 0, "ademamix": 1, "momentum": 2, "lion": 3}
+TWO_STATE = ("adam", "adamw", "ademamix")
+SCALAR_NAMES = ["lr", "b1", "b2", "eps", "wd", "omb1", "omb2", "ic1", "rs2", "decay",
+                "b3t", "omb3", "alpha_t", "max_unorm"]
+
+
+class BitoptError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class HParams(ctypes.Structure):
+    """Mirror of bitopt_hparams."""
+    _fields_ = [
+        ("optimizer", ctypes.c_int32),
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+        ("beta3", ctypes.c_float), ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+        ("alpha", ctypes.c_float),
+        ("t_alpha", ctypes.c_int32), ("t_beta3", ctypes.c_int32),
+        ("max_unorm", ctypes.c_float),
+        ("skip_zeros", ctypes.c_int32),
+        ("blocksize", ctypes.c_int32),
+    ]
+
+
+def make_hparams(hp: dict) -> HParams:
+    """bitopt_hparams from a dict; missing keys take the Optimizer2State defaults."""
+    if isinstance(hp, HParams):
+        return hp
+    h = HParams()
+    h.optimizer = OPTIMIZERS[hp["optimizer"]]
+    h.lr = hp.get("lr", 1e-3)
+    h.beta1 = hp.get("beta1", 0.9)
+    h.beta2 = hp.get("beta2", 0.999)
+    h.beta3 = hp.get("beta3", 0.9999)
+    h.eps = hp.get("eps", 1e-8)
+    h.weight_decay = hp.get("weight_decay", 0.0)
+    h.alpha = hp.get("alpha", 0.0)
+    h.t_alpha = hp.get("t_alpha") or 0
+    h.t_beta3 = hp.get("t_beta3") or 0
+    h.max_unorm = hp.get("max_unorm", 0.0)
+    h.skip_zeros = 1 if hp.get("skip_zeros", False) else 0
+    h.blocksize = hp.get("blocksize", 256)
+    return h
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "or python bit_optimizers_block_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        HP = ctypes.POINTER(HParams)
+        sigs = {
+            "bitopt_last_error": ([], ctypes.c_char_p),
+            "bitopt_abi_version": ([], i32),
+            "bitopt_create_dynamic_map": ([ctypes.c_int, P], ctypes.c_int),
+            "bitopt_step_scalars": ([HP, i32, P], ctypes.c_int),
+            "bitopt_quantize_blockwise": ([P, i32, i64, P, i32, P, P, P], ctypes.c_int),
+            "bitopt_dequantize_blockwise": ([P, P, P, i64, i32, P, i32, P], ctypes.c_int),
+            "bitopt_step_8bit_blockwise_2state": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P], ctypes.c_int),
+            "bitopt_step_8bit_blockwise_1state": ([HP, i32, P, P, i32, i64, P, P, P, P], ctypes.c_int),
+            "bitopt_step_32bit_2state": ([HP, i32, P, P, i32, i64, P, P, P], ctypes.c_int),
+            "bitopt_step_32bit_1state": ([HP, i32, P, P, i32, i64, P, P], ctypes.c_int),
+        }
+        for name, (args, res) in sigs.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().bitopt_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise BitoptError(rc, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, numel=None, device=True):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+
+
+def _dt(t):
+    if t.dtype not in DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return DTYPES[t.dtype]
+
+
+def abi_version() -> int:
+    return lib().bitopt_abi_version()
+
+
+def create_dynamic_map(signed: bool = True) -> torch.Tensor:
+    """The 256-entry dynamic-exponent codebook (host fp32 tensor)."""
+    out = torch.empty(256, dtype=torch.float32)
+    _check(lib().bitopt_create_dynamic_map(1 if signed else 0, _ptr(out)))
+    return out
+
+
+def step_scalars(hp, step: int) -> dict:
+    h = make_hparams(hp)
+    out = torch.empty(14, dtype=torch.float32)
+    _check(lib().bitopt_step_scalars(ctypes.byref(h), int(step), _ptr(out)))
+    return dict(zip(SCALAR_NAMES, out.tolist()))
+
+
+def nblocks(n: int, blocksize: int) -> int:
+    return (n + blocksize - 1) // blocksize
+
+
+def quantize_blockwise(x, qmap, blocksize: int = 256, codes=None, absmax=None, stream=None):
+    n = x.numel()
+    _need(x, "x"); _need(qmap, "qmap", torch.float32, 256)
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.uint8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty(nblocks(n, blocksize), dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8, n); _need(absmax, "absmax", torch.float32, nblocks(n, blocksize))
+    _check(lib().bitopt_quantize_blockwise(_ptr(x), _dt(x), n, _ptr(qmap), blocksize, _ptr(codes),
+                                           _ptr(absmax), _stream(stream)))
+    return codes, absmax
+
+
+def dequantize_blockwise(codes, absmax, qmap, blocksize: int = 256, out=None, dtype=torch.float32, stream=None):
+    n = codes.numel()
+    _need(codes, "codes", torch.uint8); _need(qmap, "qmap", torch.float32, 256)
+    _need(absmax, "absmax", torch.float32, nblocks(n, blocksize))
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=codes.device)
+    _need(out, "out", numel=n)
+    _check(lib().bitopt_dequantize_blockwise(_ptr(codes), _ptr(absmax), _ptr(qmap), n, blocksize,
+                                             _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+def step_8bit_blockwise_2state(hp, step, p, g, state1, state2, absmax1, absmax2, qmap1, qmap2, stream=None):
+    h = make_hparams(hp)
+    n = p.numel()
+    k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
+    nb = nblocks(n, h.blocksize)
+    _need(p, "p"); _need(g, "g", p.dtype, n)
+    _need(state1, "state1", torch.uint8, k * n); _need(state2, "state2", torch.uint8, n)
+    _need(absmax1, "absmax1", torch.float32, k * nb); _need(absmax2, "absmax2", torch.float32, nb)
+    _need(qmap1, "qmap1", torch.float32, 256); _need(qmap2, "qmap2", torch.float32, 256)
+    _check(lib().bitopt_step_8bit_blockwise_2state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
+                                                   _ptr(state1), _ptr(state2), _ptr(absmax1), _ptr(absmax2),
+                                                   _ptr(qmap1), _ptr(qmap2), _stream(stream)))
+
+
+def step_8bit_blockwise_1state(hp, step, p, g, state1, absmax1, qmap1, stream=None):
+    h = make_hparams(hp)
+    n = p.numel()
+    _need(p, "p"); _need(g, "g", p.dtype, n)
+    _need(state1, "state1", torch.uint8, n); _need(absmax1, "absmax1", torch.float32, nblocks(n, h.blocksize))
+    _need(qmap1, "qmap1", torch.float32, 256)
+    _check(lib().bitopt_step_8bit_blockwise_1state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
+                                                   _ptr(state1), _ptr(absmax1), _ptr(qmap1), _stream(stream)))
+
+
+def step_32bit_2state(hp, step, p, g, state1, state2, stream=None):
+    h = make_hparams(hp)
+    n = p.numel()
+    k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
+    _need(p, "p"); _need(g, "g", p.dtype, n)
+    _need(state1, "state1", torch.float32, k * n); _need(state2, "state2", torch.float32, n)
+    _check(lib().bitopt_step_32bit_2state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
+                                          _ptr(state1), _ptr(state2), _stream(stream)))
+
+
+def step_32bit_1state(hp, step, p, g, state1, stream=None):
+    h = make_hparams(hp)
+    n = p.numel()
+    _need(p, "p"); _need(g, "g", p.dtype, n); _need(state1, "state1", torch.float32, n)
+    _check(lib().bitopt_step_32bit_1state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
+                                          _ptr(state1), _stream(stream)))

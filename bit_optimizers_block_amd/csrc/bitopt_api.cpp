@@ -1,0 +1,255 @@
+// bitopt_api.cpp -- the C ABI of libbitopt (declared in include/bitopt.h):
+// argument checks, per-step scalars, the host codebook builder and kernel dispatch.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "bitopt.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return BITOPT_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(BITOPT_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(int32_t d) { return d == BITOPT_F32 || d == BITOPT_F16 || d == BITOPT_BF16; }
+bool valid_blocksize(int32_t b) { return b == 256 || b == 2048; }
+int elem_size(int32_t d) { return d == BITOPT_F32 ? 4 : 2; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; }
+
+// Hyper-parameter checks shared by every step entry point.
+int check_hparams(const bitopt_hparams* hp, int32_t step, int64_t n, const char* fn) {
+    if (!hp) return fail(BITOPT_ERR_INVALID_ARG, "%s: hp is NULL", fn);
+    if (hp->optimizer < BITOPT_ADAM || hp->optimizer > BITOPT_LION)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown optimizer %d", fn, hp->optimizer);
+    if (step < 1) return fail(BITOPT_ERR_INVALID_ARG, "%s: step must be >= 1 (got %d)", fn, step);
+    if (n < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: n < 0", fn);
+    if (!valid_blocksize(hp->blocksize))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: blocksize must be 256 or 2048 (got %d)", fn, hp->blocksize);
+    if (!beta_ok(hp->beta1) || !beta_ok(hp->beta2))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: betas must lie in [0, 1)", fn);
+    if (hp->optimizer == BITOPT_ADEMAMIX && !beta_ok(hp->beta3))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: beta3 must lie in [0, 1)", fn);
+    if (hp->optimizer == BITOPT_ADEMAMIX && hp->t_beta3 > 0 && !(hp->beta1 > 0.0f && hp->beta3 > 0.0f))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: a beta3 schedule needs beta1 > 0 and beta3 > 0", fn);
+    if (!(hp->eps >= 0.0f)) return fail(BITOPT_ERR_INVALID_ARG, "%s: eps < 0", fn);
+    if (!(hp->lr >= 0.0f)) return fail(BITOPT_ERR_INVALID_ARG, "%s: lr < 0", fn);
+    if (!(hp->max_unorm >= 0.0f)) return fail(BITOPT_ERR_INVALID_ARG, "%s: max_unorm < 0", fn);
+    if (!std::isfinite(hp->weight_decay) || !std::isfinite(hp->alpha))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: weight_decay and alpha must be finite", fn);
+    return BITOPT_OK;
+}
+
+// beta3(t) of AdEMAMix: the slow EMA's half-life grows linearly in t from beta1's
+// to beta3's over T steps (1/ln beta3(t) interpolates 1/ln beta1 and 1/ln beta3),
+// capped at beta3.
+double beta3_at(double b1, double b3, int32_t t, int32_t T) {
+    if (T <= 0) return b3;
+    const double l1 = std::log(b1), l3 = std::log(b3);
+    const double f = (double)t / (double)T;
+    const double v = std::exp(l1 * l3 / ((1.0 - f) * l3 + f * l1));
+    return std::min(v, b3);
+}
+
+double alpha_at(double alpha, int32_t t, int32_t T) {
+    if (T <= 0) return alpha;
+    return alpha * std::min((double)t / (double)T, 1.0);
+}
+
+bitopt::StepScalars make_scalars(const bitopt_hparams& h, int32_t t) {
+    bitopt::StepScalars s{};
+    const double b1 = h.beta1, b2 = h.beta2;
+    s.lr = h.lr; s.b1 = h.beta1; s.b2 = h.beta2; s.eps = h.eps; s.wd = h.weight_decay;
+    s.omb1 = (float)(1.0 - b1);
+    s.omb2 = (float)(1.0 - b2);
+    s.ic1 = (float)(1.0 / (1.0 - std::pow(b1, (double)t)));
+    s.rs2 = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, (double)t)));
+    s.decay = (float)(1.0 - (double)h.lr * (double)h.weight_decay);
+    const double b3t = beta3_at(b1, (double)h.beta3, t, h.t_beta3);
+    s.b3t = (float)b3t;
+    s.omb3 = (float)(1.0 - b3t);
+    s.alpha_t = (float)alpha_at((double)h.alpha, t, h.t_alpha);
+    s.max_unorm = h.max_unorm;
+    return s;
+}
+
+hipError_t dispatch_step(const bitopt::StepArgs& a, int opt, int dtype, int bs, bool quant, bool skip,
+                         bool unorm, hipStream_t s) {
+    switch (opt) {
+    case BITOPT_ADAM: return bitopt::launch_step_adam(a, dtype, bs, quant, skip, unorm, s);
+    case BITOPT_ADEMAMIX: return bitopt::launch_step_ademamix(a, dtype, bs, quant, skip, unorm, s);
+    case BITOPT_MOMENTUM: return bitopt::launch_step_momentum(a, dtype, bs, quant, skip, unorm, s);
+    default: return bitopt::launch_step_lion(a, dtype, bs, quant, skip, unorm, s);
+    }
+}
+
+int run_step(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype, int64_t n,
+             void* s1, void* s2, float* a1, float* a2, const float* q1, const float* q2, bool quant,
+             void* stream, const char* fn) {
+    bitopt::StepArgs a{};
+    a.p = p; a.g = g; a.s1 = s1; a.s2 = s2; a.a1 = a1; a.a2 = a2; a.q1 = q1; a.q2 = q2;
+    a.n = n;
+    a.nb = (n + hp->blocksize - 1) / hp->blocksize;
+    a.s = make_scalars(*hp, step);
+    const int es = elem_size(dtype);
+    const bool ademamix = hp->optimizer == BITOPT_ADEMAMIX;
+    bool vec = aligned(p, 4 * es) && aligned(g, 4 * es);
+    const uintptr_t sal = quant ? 4 : 16;               // 4 codes or 4 fp32 states per lane
+    vec = vec && aligned(s1, sal) && (!s2 || aligned(s2, sal));
+    if (ademamix) vec = vec && (n % 4 == 0);              // m2 starts n elements after m1
+    a.vec = vec ? 1 : 0;
+    hipError_t e = dispatch_step(a, hp->optimizer, dtype, hp->blocksize, quant, hp->skip_zeros != 0,
+                                 hp->max_unorm > 0.0f, reinterpret_cast<hipStream_t>(stream));
+    return device_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bitopt_last_error(void) { return g_last_error.c_str(); }
+
+int32_t bitopt_abi_version(void) { return 1; }
+
+// Signed map: per decade 10^-E (E = 0..6) the 2^(6-E) midpoints of equal bins of
+// [0.1, 1] * 10^-E, with both signs; unsigned map: 2^(7-E) midpoints per decade.
+// Both add exact 0 and +1.0.  Formed in double, rounded once to fp32, sorted.
+int bitopt_create_dynamic_map(int is_signed, float* out256) {
+    if (!out256) return fail(BITOPT_ERR_INVALID_ARG, "bitopt_create_dynamic_map: out256 is NULL");
+    const int top_bits = is_signed ? 6 : 7;
+    int k = 0;
+    out256[k++] = 0.0f;
+    out256[k++] = 1.0f;
+    for (int E = 0; E <= 6; ++E) {
+        const int bits = top_bits - E;
+        const double bins = (double)(1 << bits);
+        const double scale = std::pow(10.0, -(double)E);
+        for (int f = 0; f < (1 << bits); ++f) {
+            const double mid = 0.1 + 0.9 * ((double)f + 0.5) / bins;
+            const float v = (float)(scale * mid);
+            out256[k++] = v;
+            if (is_signed) out256[k++] = -v;
+        }
+    }
+    if (k != 256) return fail(BITOPT_ERR_DEVICE, "bitopt_create_dynamic_map: internal count %d", k);
+    std::sort(out256, out256 + 256);
+    return ok();
+}
+
+int bitopt_step_scalars(const bitopt_hparams* hp, int32_t step, float* out14) {
+    if (!out14) return fail(BITOPT_ERR_INVALID_ARG, "bitopt_step_scalars: out14 is NULL");
+    if (int rc = check_hparams(hp, step, 0, "bitopt_step_scalars")) return rc;
+    const bitopt::StepScalars s = make_scalars(*hp, step);
+    const float v[14] = {s.lr, s.b1, s.b2, s.eps, s.wd, s.omb1, s.omb2, s.ic1, s.rs2, s.decay,
+                         s.b3t, s.omb3, s.alpha_t, s.max_unorm};
+    std::memcpy(out14, v, sizeof v);
+    return ok();
+}
+
+int bitopt_quantize_blockwise(const void* x, int32_t dtype, int64_t n, const float* qmap, int32_t blocksize,
+                              uint8_t* codes, float* absmax, void* stream) {
+    const char* fn = "bitopt_quantize_blockwise";
+    if (n < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: n < 0", fn);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (!valid_blocksize(blocksize)) return fail(BITOPT_ERR_INVALID_ARG, "%s: blocksize must be 256 or 2048", fn);
+    if (n == 0) return ok();
+    if (!x || !qmap || !codes || !absmax) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    bitopt::CodecArgs a{};
+    a.x = x; a.codes = codes; a.absmax = absmax; a.qmap = qmap; a.n = n;
+    a.nb = (n + blocksize - 1) / blocksize;
+    a.vec = (aligned(x, 4 * elem_size(dtype)) && aligned(codes, 4)) ? 1 : 0;
+    return device_status(bitopt::launch_quantize(a, dtype, blocksize, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int bitopt_dequantize_blockwise(const uint8_t* codes, const float* absmax, const float* qmap, int64_t n,
+                                int32_t blocksize, void* out, int32_t dtype, void* stream) {
+    const char* fn = "bitopt_dequantize_blockwise";
+    if (n < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: n < 0", fn);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (!valid_blocksize(blocksize)) return fail(BITOPT_ERR_INVALID_ARG, "%s: blocksize must be 256 or 2048", fn);
+    if (n == 0) return ok();
+    if (!codes || !absmax || !qmap || !out) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    bitopt::CodecArgs a{};
+    a.out = out; a.codes = const_cast<uint8_t*>(codes); a.absmax = const_cast<float*>(absmax); a.qmap = qmap;
+    a.n = n;
+    a.nb = (n + blocksize - 1) / blocksize;
+    a.vec = (aligned(out, 4 * elem_size(dtype)) && aligned(codes, 4)) ? 1 : 0;
+    return device_status(bitopt::launch_dequantize(a, dtype, blocksize, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int bitopt_step_8bit_blockwise_2state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                      int32_t dtype, int64_t n, uint8_t* state1, uint8_t* state2,
+                                      float* absmax1, float* absmax2, const float* qmap1,
+                                      const float* qmap2, void* stream) {
+    const char* fn = "bitopt_step_8bit_blockwise_2state";
+    if (int rc = check_hparams(hp, step, n, fn)) return rc;
+    if (hp->optimizer != BITOPT_ADAM && hp->optimizer != BITOPT_ADEMAMIX)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: optimizer %d is not a 2-state optimizer", fn, hp->optimizer);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (n == 0) return ok();
+    if (!p || !g || !state1 || !state2 || !absmax1 || !absmax2 || !qmap1 || !qmap2)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    return run_step(hp, step, p, g, dtype, n, state1, state2, absmax1, absmax2, qmap1, qmap2, true, stream, fn);
+}
+
+int bitopt_step_8bit_blockwise_1state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                      int32_t dtype, int64_t n, uint8_t* state1, float* absmax1,
+                                      const float* qmap1, void* stream) {
+    const char* fn = "bitopt_step_8bit_blockwise_1state";
+    if (int rc = check_hparams(hp, step, n, fn)) return rc;
+    if (hp->optimizer != BITOPT_MOMENTUM && hp->optimizer != BITOPT_LION)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: optimizer %d is not a 1-state optimizer", fn, hp->optimizer);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (n == 0) return ok();
+    if (!p || !g || !state1 || !absmax1 || !qmap1) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    return run_step(hp, step, p, g, dtype, n, state1, nullptr, absmax1, nullptr, qmap1, nullptr, true, stream, fn);
+}
+
+int bitopt_step_32bit_2state(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype,
+                             int64_t n, float* state1, float* state2, void* stream) {
+    const char* fn = "bitopt_step_32bit_2state";
+    if (int rc = check_hparams(hp, step, n, fn)) return rc;
+    if (hp->optimizer != BITOPT_ADAM && hp->optimizer != BITOPT_ADEMAMIX)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: optimizer %d is not a 2-state optimizer", fn, hp->optimizer);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (n == 0) return ok();
+    if (!p || !g || !state1 || !state2) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    return run_step(hp, step, p, g, dtype, n, state1, state2, nullptr, nullptr, nullptr, nullptr, false, stream, fn);
+}
+
+int bitopt_step_32bit_1state(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype,
+                             int64_t n, float* state1, void* stream) {
+    const char* fn = "bitopt_step_32bit_1state";
+    if (int rc = check_hparams(hp, step, n, fn)) return rc;
+    if (hp->optimizer != BITOPT_MOMENTUM && hp->optimizer != BITOPT_LION)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: optimizer %d is not a 1-state optimizer", fn, hp->optimizer);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (n == 0) return ok();
+    if (!p || !g || !state1) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    return run_step(hp, step, p, g, dtype, n, state1, nullptr, nullptr, nullptr, nullptr, nullptr, false, stream, fn);
+}
+
+}  // extern "C"

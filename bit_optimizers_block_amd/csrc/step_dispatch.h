@@ -1,0 +1,40 @@
+// step_dispatch.h -- maps the run-time (dtype, blocksize, mode, flags) of a step
+// call to its kernel instantiation.  Included once per optimizer family, so each
+// family's kernels compile in their own translation unit.
+#pragma once
+
+#include "launch.h"
+
+namespace bitopt {
+
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM>
+hipError_t launch_one(const StepArgs& a, hipStream_t s) {
+    constexpr int64_t tile = (int64_t)TileChunks<BS>::v * 256;
+    hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM>), tile_grid(a.n, tile), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DT, int OPT, int BS, bool QUANT>
+hipError_t launch_flags(const StepArgs& a, bool skip, bool unorm, hipStream_t s) {
+    if (skip) return unorm ? launch_one<DT, OPT, BS, QUANT, true, true>(a, s) : launch_one<DT, OPT, BS, QUANT, true, false>(a, s);
+    return unorm ? launch_one<DT, OPT, BS, QUANT, false, true>(a, s) : launch_one<DT, OPT, BS, QUANT, false, false>(a, s);
+}
+
+template <int DT, int OPT>
+hipError_t launch_bs(const StepArgs& a, int bs, bool quant, bool skip, bool unorm, hipStream_t s) {
+    if (bs == 256) return quant ? launch_flags<DT, OPT, 256, true>(a, skip, unorm, s) : launch_flags<DT, OPT, 256, false>(a, skip, unorm, s);
+    if (bs == 2048) return quant ? launch_flags<DT, OPT, 2048, true>(a, skip, unorm, s) : launch_flags<DT, OPT, 2048, false>(a, skip, unorm, s);
+    return hipErrorInvalidValue;
+}
+
+template <int OPT>
+hipError_t launch_step_family(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s) {
+    switch (dtype) {
+    case kF32: return launch_bs<kF32, OPT>(a, bs, quant, skip, unorm, s);
+    case kF16: return launch_bs<kF16, OPT>(a, bs, quant, skip, unorm, s);
+    case kBF16: return launch_bs<kBF16, OPT>(a, bs, quant, skip, unorm, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace bitopt

@@ -1,0 +1,196 @@
+/*
+ * bitopt.h -- C ABI of libbitopt, the MI355X (gfx950) 8-bit block-wise optimizer step.
+ *
+ * The method: optimizer state is held as one byte per element, a code into a
+ * 256-entry non-linear "dynamic exponent" codebook, scaled by one fp32 absmax per
+ * block of `blocksize` elements ("8-bit Optimizers via Block-wise Quantization",
+ * abstract; the k-bit scaling-laws quote in its citing-papers section).  One step
+ * decodes each block, applies the optimizer update in fp32, recomputes the block
+ * absmax and re-encodes to the nearest code.  The hyper-parameters mirror the
+ * Optimizer2State / Optimizer1State lists of the bitsandbytes "optim_overview"
+ * page; the state layout mirrors the state-name table of the "[XPU] Implemented
+ * 8bit optimizers in triton #1692" benchmark script; skip_zeros follows "Support
+ * skip_zeros in the XPU Triton optimizer kernels #2097".
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns a status code (BITOPT_OK or a negative BITOPT_ERR_*).  On
+ *     error, bitopt_last_error() returns a message (per calling thread).  No C++
+ *     exception crosses this interface.
+ *   - Pointers named as device pointers are caller-owned device memory on the
+ *     current HIP device.  The library never allocates, frees or retains caller
+ *     memory.  `stream` is a hipStream_t (NULL = the null stream); calls enqueue
+ *     work on it and return without waiting.  Launch errors are returned at once;
+ *     faults during execution surface at the caller's next synchronisation.
+ *   - n == 0 is a successful no-op.  Arguments are checked before anything is
+ *     enqueued: n < 0, a NULL pointer that the call needs, an unknown dtype or
+ *     optimizer, a blocksize other than 256 or 2048, step < 1, a beta outside
+ *     [0, 1), eps < 0, lr < 0 or max_unorm < 0 give BITOPT_ERR_INVALID_ARG.
+ *   - Any alignment is accepted; buffers aligned to 16 bytes take the vector path.
+ *   - Calls are stateless and re-entrant.  Fresh state buffers are zero-filled:
+ *     codes 0 and absmax 0 decode to zero.
+ *   - Element arithmetic is IEEE fp32 (no contraction to FMA, correctly rounded
+ *     division and square root); per-step scalars (bias corrections, schedules,
+ *     1 - beta, 1 - lr*wd) are formed in double and rounded once to fp32.
+ *     Results are deterministic run to run (no atomics).
+ */
+#ifndef BITOPT_H
+#define BITOPT_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define BITOPT_API __attribute__((visibility("default")))
+#else
+#define BITOPT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BITOPT_OK 0
+#define BITOPT_ERR_INVALID_ARG (-1)
+#define BITOPT_ERR_UNSUPPORTED (-2)
+#define BITOPT_ERR_DEVICE (-3)
+
+/* Element types of parameters, gradients and codec inputs/outputs. */
+#define BITOPT_F32 0
+#define BITOPT_F16 1
+#define BITOPT_BF16 2
+
+/* Optimizers.  ADAM covers Adam and AdamW (decoupled decay when weight_decay > 0). */
+#define BITOPT_ADAM 0
+#define BITOPT_ADEMAMIX 1
+#define BITOPT_MOMENTUM 2
+#define BITOPT_LION 3
+
+/*
+ * Hyper-parameters of one step ("optim_overview": Optimizer2State and
+ * Optimizer1State argument lists).  Defaults there: lr 1e-3, betas (0.9, 0.999),
+ * eps 1e-8, weight_decay 0, max_unorm 0 (off), skip_zeros false, alpha 0,
+ * t_alpha / t_beta3 None (here: <= 0).
+ *   optimizer     BITOPT_ADAM | BITOPT_ADEMAMIX | BITOPT_MOMENTUM | BITOPT_LION
+ *   beta1, beta2  Adam/AdEMAMix EMA rates; Momentum uses beta1 as the momentum;
+ *                 Lion uses beta1 for the update interpolation, beta2 for its EMA.
+ *   beta3, alpha  AdEMAMix slow EMA rate and mixing weight.
+ *   t_alpha, t_beta3  AdEMAMix warm-up lengths for alpha and beta3 (<= 0: none).
+ *   weight_decay  decoupled (p *= 1 - lr*wd) for Adam/AdEMAMix/Lion; added to the
+ *                 gradient (g + wd*p) for Momentum.
+ *   max_unorm     > 0: per block, the update's L2 norm is capped at max_unorm times
+ *                 the block's parameter L2 norm.
+ *   skip_zeros    != 0: elements whose raw gradient is exactly +-0 keep their
+ *                 parameter bits; a block whose every gradient is zero is not
+ *                 written at all (codes, absmax, parameters untouched).
+ *   blocksize     256 or 2048 elements per absmax block.
+ */
+typedef struct bitopt_hparams {
+    int32_t optimizer;
+    float lr, beta1, beta2, beta3, eps, weight_decay, alpha;
+    int32_t t_alpha, t_beta3;
+    float max_unorm;
+    int32_t skip_zeros;
+    int32_t blocksize;
+} bitopt_hparams;
+
+/* Message describing the last error on the calling thread ("" if none). */
+BITOPT_API const char* bitopt_last_error(void);
+
+/* ABI version of this header (increments on incompatible changes). */
+BITOPT_API int32_t bitopt_abi_version(void);
+
+/*
+ * Host-only.  Writes the 256-entry dynamic-exponent codebook, sorted ascending,
+ * into out256 (host memory).  is_signed != 0: the signed map (sign bit, then a run
+ * of zero bits selecting the decade 10^-E, an indicator bit and 6-E linear
+ * fraction bits; used for first moments).  is_signed == 0: the unsigned map (no
+ * sign bit, 7-E fraction bits; used for second moments).  Each pattern stands for
+ * the midpoint of its bin; exact 0 and +1.0 are included.  A code is an index
+ * into this array.  ("8-bit Optimizers via Block-wise Quantization": abstract and
+ * the dynamic-exponent quote among its citing papers.)
+ */
+BITOPT_API int bitopt_create_dynamic_map(int is_signed, float* out256);
+
+/*
+ * Host-only.  The fp32 per-step scalars the step kernels use for `step`, in this
+ * order: lr, beta1, beta2, eps, weight_decay, 1-beta1, 1-beta2, 1/(1-beta1^t),
+ * 1/sqrt(1-beta2^t), 1-lr*weight_decay, beta3(t), 1-beta3(t), alpha(t), max_unorm.
+ * Each is formed in double from the fp32 fields of hp and rounded once.  AdEMAMix
+ * ("optim_overview": alpha, t_alpha, t_beta3): alpha(t) = alpha*min(t/t_alpha, 1);
+ * beta3(t) moves the slow EMA's half-life linearly from beta1's to beta3's over
+ * t_beta3 steps, capped at beta3.  out14: host, 14 floats.
+ */
+BITOPT_API int bitopt_step_scalars(const bitopt_hparams* hp, int32_t step, float* out14);
+
+/*
+ * Block-wise quantization ("8-bit Optimizers via Block-wise Quantization",
+ * abstract).  For each block b of `blocksize` elements of x (device, `dtype`):
+ * absmax[b] = max |x| over the block's valid elements, then every element gets
+ * the index of the nearest qmap entry to x * (1/absmax[b]) (fp32 distance; ties to
+ * the lower index; an all-zero block encodes to the code of 0.0).
+ *   x        device, n elements of dtype
+ *   qmap     device, 256 fp32 sorted ascending
+ *   codes    device, n bytes (written)
+ *   absmax   device, ceil(n/blocksize) fp32 (written)
+ */
+BITOPT_API int bitopt_quantize_blockwise(const void* x, int32_t dtype, int64_t n, const float* qmap,
+                              int32_t blocksize, uint8_t* codes, float* absmax, void* stream);
+
+/*
+ * Block-wise dequantization, as dequantize_blockwise(code, absmax, A, blocksize)
+ * in the "#1692" test script: out[i] = qmap[codes[i]] * absmax[i / blocksize],
+ * one fp32 multiply, rounded to nearest-even into `dtype`.
+ *   codes n bytes, absmax ceil(n/blocksize) fp32, qmap 256 fp32, out n of dtype
+ *   (all device).
+ */
+BITOPT_API int bitopt_dequantize_blockwise(const uint8_t* codes, const float* absmax, const float* qmap,
+                                int64_t n, int32_t blocksize, void* out, int32_t dtype, void* stream);
+
+/*
+ * Fused 8-bit block-wise step of a 2-state optimizer (Optimizer2State): Adam/AdamW
+ * or AdEMAMix.  One pass: decode, update, new absmax, re-encode, write p.
+ *   hp      host pointer; optimizer must be BITOPT_ADAM or BITOPT_ADEMAMIX
+ *   step    1-based step count t (bias corrections and schedules use it)
+ *   p       device, n elements of dtype (read and written)
+ *   g       device, n elements of dtype (read)
+ *   state1  device uint8 codes of the first moment: n bytes (Adam: exp_avg);
+ *           AdEMAMix: 2n bytes, fast EMA m1 then slow EMA m2
+ *   state2  device uint8 codes of the second moment, n bytes (exp_avg_sq / nu)
+ *   absmax1 device fp32, nb = ceil(n/blocksize) entries (AdEMAMix: 2*nb, m1's then m2's)
+ *   absmax2 device fp32, nb entries
+ *   qmap1   device fp32[256], signed map (shared by m1 and m2)
+ *   qmap2   device fp32[256], unsigned map
+ */
+BITOPT_API int bitopt_step_8bit_blockwise_2state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                      int32_t dtype, int64_t n, uint8_t* state1, uint8_t* state2,
+                                      float* absmax1, float* absmax2, const float* qmap1,
+                                      const float* qmap2, void* stream);
+
+/*
+ * Fused 8-bit block-wise step of a 1-state optimizer (Optimizer1State): Momentum
+ * (state1 = momentum_buffer) or Lion (state1 = exp_avg).  Arguments as above with
+ * one state: state1 n bytes, absmax1 nb fp32, qmap1 the signed map.
+ */
+BITOPT_API int bitopt_step_8bit_blockwise_1state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                      int32_t dtype, int64_t n, uint8_t* state1, float* absmax1,
+                                      const float* qmap1, void* stream);
+
+/*
+ * 32-bit steps: the same updates with fp32 states and no codec -- the path for
+ * tensors below min_8bit_size ("optim_overview": min_8bit_size, default 4096) and
+ * the 32-bit optimizers the 8-bit ones are compared against.
+ *   2-state: state1 fp32 n (Adam: m; AdEMAMix: 2n, m1 then m2), state2 fp32 n (v / nu)
+ *   1-state: state1 fp32 n
+ * skip_zeros leaves the states of zero-gradient elements untouched; max_unorm
+ * groups elements in blocks of hp->blocksize.
+ */
+BITOPT_API int bitopt_step_32bit_2state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                             int32_t dtype, int64_t n, float* state1, float* state2, void* stream);
+BITOPT_API int bitopt_step_32bit_1state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                             int32_t dtype, int64_t n, float* state1, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITOPT_H */

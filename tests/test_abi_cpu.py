@@ -1,0 +1,127 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every symbol the
+header declares, and its host-only logic (codebook builder, per-step scalars,
+argument checks) agrees with the oracle and with the header's contract.  No call
+here reaches a kernel launch: every device entry point is exercised only on its
+argument-checking paths and with n == 0.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitopt.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from bit_optimizers_block_amd import bitopt
+    if not os.path.exists(bitopt.LIB_PATH):
+        from bit_optimizers_block_amd import build
+        build.build()
+    bitopt.lib()
+    return bitopt
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"BITOPT_API\s+[\w\s\*]+?\b(bitopt_\w+)\s*\(", src)
+
+
+def test_exports_every_declared_symbol(B):
+    names = declared_functions()
+    assert len(names) >= 10
+    L = ctypes.CDLL(B.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in bitopt.h but not exported"
+    assert B.abi_version() == 1
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "bitopt.h"\nint main(void){bitopt_hparams h; (void)h; return BITOPT_OK;}\n')
+    import subprocess
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{os.path.dirname(HEADER)}", "-c", str(src),
+                    "-o", str(tmp_path / "use.o")], check=True)
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_codebook_equals_oracle(B, oref, signed):
+    mine = B.create_dynamic_map(signed).numpy()
+    np.testing.assert_array_equal(mine.view(np.uint32), oref.dynamic_map(signed).view(np.uint32))
+
+
+HP_CASES = [
+    dict(optimizer="adam", lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01),
+    dict(optimizer="adam", lr=3e-4, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1),
+    dict(optimizer="ademamix", lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, t_alpha=100, t_beta3=100),
+    dict(optimizer="ademamix", lr=1e-3, beta3=0.999, alpha=8.0),
+    dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01),
+    dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01),
+]
+
+
+@pytest.mark.parametrize("hp", HP_CASES)
+def test_step_scalars_equal_oracle(B, oref, hp):
+    for t in (1, 2, 7, 50, 99, 100, 101, 1000, 100000):
+        mine = B.step_scalars(hp, t)
+        ref = oref.step_scalars(hp, t)
+        for k, v in ref.items():
+            assert np.float32(mine[k]) == np.float32(v), (k, t, mine[k], v)
+
+
+def _call2(B, hp=None, step=1, n=16, dtype=0, ptr=16, nulls=()):
+    h = B.make_hparams(hp or dict(optimizer="adam"))
+    P = [ctypes.c_void_p(None if i in nulls else ptr) for i in range(8)]
+    return B.lib().bitopt_step_8bit_blockwise_2state(ctypes.byref(h), step, P[0], P[1], dtype, n, P[2], P[3],
+                                                     P[4], P[5], P[6], P[7], None)
+
+
+def test_argument_errors(B):
+    E = B.ERR_INVALID_ARG
+    assert _call2(B, n=0) == B.OK                                      # empty: no-op
+    assert _call2(B, n=-1) == E
+    assert _call2(B, step=0) == E and "step" in B.last_error()
+    assert _call2(B, dtype=7) == E and "dtype" in B.last_error()
+    assert _call2(B, nulls=(3,)) == E and "NULL" in B.last_error()
+    assert _call2(B, hp=dict(optimizer="adam", blocksize=512)) == E and "blocksize" in B.last_error()
+    assert _call2(B, hp=dict(optimizer="adam", beta1=1.0)) == E
+    assert _call2(B, hp=dict(optimizer="adam", beta2=-0.1)) == E
+    assert _call2(B, hp=dict(optimizer="adam", eps=-1.0)) == E
+    assert _call2(B, hp=dict(optimizer="adam", max_unorm=-1.0)) == E
+    assert _call2(B, hp=dict(optimizer="momentum")) == E and "2-state" in B.last_error()
+    h = B.make_hparams(dict(optimizer="adam"))
+    h.optimizer = 9
+    rc = B.lib().bitopt_step_8bit_blockwise_2state(ctypes.byref(h), 1, *([ctypes.c_void_p(16)] * 2), 0, 16,
+                                                   *([ctypes.c_void_p(16)] * 6), None)
+    assert rc == E and "optimizer" in B.last_error()
+    # 1-state entry points refuse 2-state optimizers and vice versa
+    h = B.make_hparams(dict(optimizer="adam"))
+    P = ctypes.c_void_p(16)
+    assert B.lib().bitopt_step_8bit_blockwise_1state(ctypes.byref(h), 1, P, P, 0, 16, P, P, P, None) == E
+    assert B.lib().bitopt_step_32bit_1state(ctypes.byref(h), 1, P, P, 0, 16, P, None) == E
+    h = B.make_hparams(dict(optimizer="lion"))
+    assert B.lib().bitopt_step_32bit_2state(ctypes.byref(h), 1, P, P, 0, 16, P, P, None) == E
+    assert B.lib().bitopt_step_8bit_blockwise_1state(ctypes.byref(h), 1, P, P, 0, 0, P, P, P, None) == B.OK
+    # codec
+    L = B.lib()
+    assert L.bitopt_quantize_blockwise(P, 0, 0, P, 256, P, P, None) == B.OK
+    assert L.bitopt_quantize_blockwise(P, 0, 10, P, 100, P, P, None) == E
+    assert L.bitopt_quantize_blockwise(P, 3, 10, P, 256, P, P, None) == E
+    assert L.bitopt_quantize_blockwise(None, 0, 10, P, 256, P, P, None) == E
+    assert L.bitopt_dequantize_blockwise(P, P, P, -5, 256, P, 0, None) == E
+    assert L.bitopt_dequantize_blockwise(P, P, None, 5, 256, P, 0, None) == E
+    assert L.bitopt_create_dynamic_map(1, None) == E
+    assert L.bitopt_step_scalars(None, 1, P) == E
+    # a successful call clears the message
+    assert L.bitopt_create_dynamic_map(1, (ctypes.c_float * 256)()) == B.OK and B.last_error() == ""
+
+
+def test_binding_refuses_host_tensors(B):
+    import torch
+    p = torch.zeros(16)
+    with pytest.raises(ValueError):
+        B.step_8bit_blockwise_1state(dict(optimizer="lion"), 1, p, p, torch.zeros(16, dtype=torch.uint8),
+                                     torch.zeros(1), torch.zeros(256))

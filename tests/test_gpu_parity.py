@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case starts both sides from the same seeded inputs; the oracle runs its own
+trajectory (it never takes data produced by the HIP path) and the two are
+compared after every step to the bar in tests/parity.py.  Sizes span several
+tiles and a ragged tail; both block sizes, all three parameter dtypes and all four
+optimizers are covered, with skip_zeros, max_unorm, the 32-bit mode, the codec,
+unaligned buffers and empty inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_optimizers_block_amd import bitopt
+from bit_optimizers_block_amd import workloads as W
+from parity import Compare, Quant8, as_f32, param_rtol, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+OPTS = {
+    "adam": dict(optimizer="adam", lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01),
+    "ademamix": dict(optimizer="ademamix", lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0,
+                     t_alpha=3, t_beta3=3, eps=1e-8, weight_decay=0.01),
+    "momentum": dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01),
+    "lion": dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    bitopt.lib()          # a missing library is an error on a GPU machine, not a skip
+
+
+def _grad(seed, t, n, dtype, zero_frac=0.0, B=256):
+    g = W.normal_f32([seed, 2, t], n, 0.01)
+    if zero_frac:
+        rng = np.random.default_rng([seed, t])
+        g[rng.random(n) < zero_frac] = 0.0
+        nb = (n + B - 1) // B
+        for b in rng.choice(nb, max(1, nb // 3), replace=False):
+            g[b * B:(b + 1) * B] = 0.0
+    return W.to_dtype(g, dtype)
+
+
+def _run(hp, n, dtype, steps, seed, zero_frac=0.0):
+    print(f"\n[case] {hp['optimizer']} {dtype} B={hp['blocksize']} n={n} steps={steps} "
+          f"skip={hp.get('skip_zeros', False)} max_unorm={hp.get('max_unorm', 0.0)}", flush=True)
+    p0 = W.to_dtype(W.normal_f32([seed, 1], n, 0.02), dtype)
+    q = Quant8(hp, p0, dtype)
+    cmp = Compare()
+    for t in range(1, steps + 1):
+        g = _grad(seed, t, n, dtype, zero_frac, hp["blocksize"])
+        q.step_gpu(t, to_dev(g, dtype))
+        q.step_oracle(t, g)
+        q.compare(cmp, f"step {t}")
+    print("  " + cmp.summary(), flush=True)
+    return cmp
+
+
+RAGGED = {256: 5 * 1024 + 300 + 5, 2048: 5 * 2048 + 1500 + 3}
+
+
+@pytest.mark.parametrize("bs", [256, 2048])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("name", list(OPTS))
+def test_step_8bit(name, dtype, bs):
+    _run(dict(OPTS[name], blocksize=bs), RAGGED[bs], dtype, 4, 100 + bs)
+
+
+@pytest.mark.parametrize("bs", [256, 2048])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("name", list(OPTS))
+def test_step_8bit_skip_zeros(name, dtype, bs):
+    _run(dict(OPTS[name], blocksize=bs, skip_zeros=True), RAGGED[bs], dtype, 4, 200 + bs, zero_frac=0.3)
+
+
+@pytest.mark.parametrize("name", list(OPTS))
+def test_step_8bit_max_unorm(name):
+    _run(dict(OPTS[name], blocksize=256, max_unorm=0.002), RAGGED[256], "f32", 3, 300)
+
+
+@pytest.mark.parametrize("n", [1, 3, 255, 256, 257, 1023, 1025, 2047, 2049])
+def test_small_and_ragged_sizes(n):
+    for bs in (256, 2048):
+        _run(dict(OPTS["adam"], blocksize=bs), n, "f32", 2, 400 + n)
+        _run(dict(OPTS["ademamix"], blocksize=bs), n, "bf16", 2, 500 + n)
+
+
+def test_empty_is_noop():
+    for name in OPTS:
+        hp = dict(OPTS[name], blocksize=256)
+        q = Quant8(hp, np.zeros(0, np.float32), "f32")
+        g = torch.zeros(0, device="cuda")
+        q.step_gpu(1, g)
+    torch.cuda.synchronize()
+
+
+def test_unaligned_buffers():
+    """Buffers that start one element / one byte off a 16-byte boundary take the
+    element-wise path and still match."""
+    n, bs = RAGGED[256], 256
+    for name, dtype in (("adam", "f32"), ("ademamix", "f16"), ("lion", "bf16")):
+        hp = dict(OPTS[name], blocksize=bs)
+        p0 = W.to_dtype(W.normal_f32([600, 1], n, 0.02), dtype)
+        q = Quant8(hp, p0, dtype)
+        for key in ("p", "s1", "s2"):
+            if key in q.d:
+                t = q.d[key]
+                big = torch.zeros(t.numel() + 1, dtype=t.dtype, device="cuda")
+                big[1:].copy_(t)
+                q.d[key] = big[1:]
+                assert q.d[key].data_ptr() % 4 != 0 or t.element_size() == 4
+        cmp = Compare()
+        for t in range(1, 4):
+            g = _grad(600, t, n, dtype)
+            gd = torch.zeros(n + 1, dtype=q.d["p"].dtype, device="cuda")
+            gd[1:].copy_(to_dev(g, dtype))
+            q.step_gpu(t, gd[1:])
+            q.step_oracle(t, g)
+            q.compare(cmp, f"{name} step {t}")
+        print(f"\n[unaligned {name} {dtype}] " + cmp.summary())
+
+
+def test_deterministic():
+    n, hp = 4 * 4096 + 77, dict(OPTS["ademamix"], blocksize=256)
+    p0 = W.to_dtype(W.normal_f32([700, 1], n, 0.02), "bf16")
+    outs = []
+    for _ in range(2):
+        q = Quant8(hp, p0, "bf16")
+        for t in range(1, 4):
+            q.step_gpu(t, to_dev(_grad(700, t, n, "bf16"), "bf16"))
+        torch.cuda.synchronize()
+        outs.append({k: to_host(v) for k, v in q.d.items()})
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k], outs[1][k])
+
+
+# ------------------------------------------------------------------ 32-bit mode
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(OPTS))
+def test_step_32bit(name, dtype):
+    n = RAGGED[256]
+    hp = dict(OPTS[name], blocksize=256, skip_zeros=(name == "lion"))
+    two = oracle.NUM_STATES[name] >= 2
+    k1 = 2 if name == "ademamix" else 1
+    p0 = W.to_dtype(W.normal_f32([800, 1], n, 0.02), dtype)
+    op, os1, os2 = p0.copy(), np.zeros(k1 * n, np.float32), np.zeros(n, np.float32) if two else None
+    dp, ds1 = to_dev(p0, dtype), torch.zeros(k1 * n, device="cuda")
+    ds2 = torch.zeros(n, device="cuda") if two else None
+    cmp = Compare()
+    for t in range(1, 5):
+        g = _grad(800, t, n, dtype, zero_frac=0.2 if hp["skip_zeros"] else 0.0)
+        if two:
+            bitopt.step_32bit_2state(hp, t, dp, to_dev(g, dtype), ds1, ds2)
+        else:
+            bitopt.step_32bit_1state(hp, t, dp, to_dev(g, dtype), ds1)
+        oracle.step_32bit(hp, t, op, g, dtype, os1, os2)
+        torch.cuda.synchronize()
+        cmp.values(as_f32(to_host(dp, dtype), dtype), as_f32(op, dtype), param_rtol(dtype), "p")
+        cmp.values(to_host(ds1), os1, 1e-6, "state1", kind="a")
+        if two:
+            cmp.values(to_host(ds2), os2, 1e-6, "state2", kind="a")
+    print(f"\n[32bit {name} {dtype}] " + cmp.summary())
+
+
+# ------------------------------------------------------------------ codec
+
+@pytest.mark.parametrize("bs", [256, 2048])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_codec(dtype, bs):
+    for signed in (True, False):
+        n = RAGGED[bs]
+        x = W.normal_f32([900, bs], n, 0.01)
+        if not signed:
+            x = np.abs(x)
+        x[: bs] = 0.0                                  # an all-zero block
+        x = W.to_dtype(x, dtype)
+        qmap = oracle.dynamic_map(signed)
+        codes_ref, absmax_ref = oracle.quantize_blockwise(x, dtype, qmap, bs)
+        qd = bitopt.create_dynamic_map(signed).cuda()
+        codes, absmax = bitopt.quantize_blockwise(to_dev(x, dtype), qd, bs)
+        cmp = Compare()
+        cmp.codes(to_host(codes), codes_ref, "codes")
+        cmp.values(to_host(absmax), absmax_ref, 1e-6, "absmax", kind="a")
+        assert cmp.bit_exact, cmp.summary()
+        out = bitopt.dequantize_blockwise(to_dev(codes_ref), to_dev(absmax_ref), qd, bs,
+                                          dtype={"f32": torch.float32, "f16": torch.float16,
+                                                 "bf16": torch.bfloat16}[dtype])
+        ref = oracle.dequantize_blockwise(codes_ref, absmax_ref, qmap, bs, dtype)
+        np.testing.assert_array_equal(to_host(out, dtype), ref)
+
+
+def test_codec_unaligned_and_empty():
+    n, bs = 3000, 256
+    x = W.normal_f32([901, 1], n, 0.01)
+    qmap = oracle.dynamic_map(True)
+    codes_ref, absmax_ref = oracle.quantize_blockwise(x[1:], "f32", qmap, bs)
+    xd = to_dev(x)[1:]
+    qd = bitopt.create_dynamic_map(True).cuda()
+    cbuf = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    codes, absmax = bitopt.quantize_blockwise(xd, qd, bs, codes=cbuf[1:])
+    np.testing.assert_array_equal(to_host(codes), codes_ref)
+    np.testing.assert_array_equal(to_host(absmax), absmax_ref)
+    e = torch.zeros(0, device="cuda")
+    bitopt.quantize_blockwise(e, qd, bs)
+    bitopt.dequantize_blockwise(torch.zeros(0, dtype=torch.uint8, device="cuda"),
+                                torch.zeros(0, device="cuda"), qd, bs)
+    torch.cuda.synchronize()
