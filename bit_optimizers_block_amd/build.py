@@ -17,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
+GEN = os.path.join(BUILD, "gen")
 LIB = os.path.join(PKG, "libbitopt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -26,7 +27,7 @@ FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
-    f"-I{INCLUDE}", f"-I{CSRC}",
+    f"-I{INCLUDE}", f"-I{CSRC}", f"-I{GEN}",
 ]
 
 SOURCES = ["bitopt_api.cpp", "codec.hip", "step_adam.hip", "step_ademamix.hip",
@@ -44,8 +45,21 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
+def generate_tables() -> str:
+    """Compile and run the host generator of the standard maps' search tables."""
+    os.makedirs(GEN, exist_ok=True)
+    exe = os.path.join(BUILD, "gen_tables")
+    cmd = ["g++", "-O2", "-std=c++17", f"-I{CSRC}", os.path.join(CSRC, "gen_tables.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True)
+    out = os.path.join(GEN, "bitopt_tables.h")
+    subprocess.run([exe, out], check=True)
+    return out
+
+
 def build(jobs: int = 8, extra=()) -> str:
-    """Compile every HIP source and link libbitopt.so; returns its path."""
+    """Generate the search tables, compile every HIP source and link libbitopt.so;
+    returns its path."""
+    generate_tables()
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + ".tmp"

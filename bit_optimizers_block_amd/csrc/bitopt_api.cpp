@@ -1,6 +1,8 @@
 // bitopt_api.cpp -- the C ABI of libbitopt (declared in include/bitopt.h):
 // argument checks, per-step scalars, the host codebook builder and kernel dispatch.
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -8,6 +10,7 @@
 #include <string>
 
 #include "bitopt.h"
+#include "dynamic_map.h"
 #include "launch.h"
 
 namespace {
@@ -96,6 +99,35 @@ bitopt::StepScalars make_scalars(const bitopt_hparams& h, int32_t t) {
     return s;
 }
 
+}  // namespace
+
+namespace bitopt {
+
+// Compute units of each device, queried on first use.  Groups per CU: enough
+// 4-wave groups to fill the CU at the step kernels' occupancy with a few tiles per
+// wave, so the LDS codebook staging is paid a few times per CU, not per tile.
+int64_t group_cap() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cus[kMaxDev];
+    static const int per_cu = [] {
+        const char* e = std::getenv("BITOPT_GROUPS_PER_CU");
+        const int v = e ? std::atoi(e) : 0;
+        return v > 0 ? v : 4;
+    }();
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 2048;
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return (int64_t)c * per_cu;
+}
+
+}  // namespace bitopt
+
+namespace {
+
 hipError_t dispatch_step(const bitopt::StepArgs& a, int opt, int dtype, int bs, bool quant, bool skip,
                          bool unorm, hipStream_t s) {
     switch (opt) {
@@ -116,10 +148,10 @@ int run_step(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int
     a.s = make_scalars(*hp, step);
     const int es = elem_size(dtype);
     const bool ademamix = hp->optimizer == BITOPT_ADEMAMIX;
-    bool vec = aligned(p, 4 * es) && aligned(g, 4 * es);
-    const uintptr_t sal = quant ? 4 : 16;               // 4 codes or 4 fp32 states per lane
-    vec = vec && aligned(s1, sal) && (!s2 || aligned(s2, sal));
-    if (ademamix) vec = vec && (n % 4 == 0);              // m2 starts n elements after m1
+    // Vector path: 4 parameters per access, codes in 16-byte words, fp32 states in
+    // 16-byte words; AdEMAMix's m2 starts n elements after m1.
+    bool vec = aligned(p, 4 * es) && aligned(g, 4 * es) && aligned(s1, 16) && (!s2 || aligned(s2, 16));
+    if (ademamix) vec = vec && (n % 16 == 0);
     a.vec = vec ? 1 : 0;
     hipError_t e = dispatch_step(a, hp->optimizer, dtype, hp->blocksize, quant, hp->skip_zeros != 0,
                                  hp->max_unorm > 0.0f, reinterpret_cast<hipStream_t>(stream));
@@ -134,28 +166,9 @@ const char* bitopt_last_error(void) { return g_last_error.c_str(); }
 
 int32_t bitopt_abi_version(void) { return 1; }
 
-// Signed map: per decade 10^-E (E = 0..6) the 2^(6-E) midpoints of equal bins of
-// [0.1, 1] * 10^-E, with both signs; unsigned map: 2^(7-E) midpoints per decade.
-// Both add exact 0 and +1.0.  Formed in double, rounded once to fp32, sorted.
 int bitopt_create_dynamic_map(int is_signed, float* out256) {
     if (!out256) return fail(BITOPT_ERR_INVALID_ARG, "bitopt_create_dynamic_map: out256 is NULL");
-    const int top_bits = is_signed ? 6 : 7;
-    int k = 0;
-    out256[k++] = 0.0f;
-    out256[k++] = 1.0f;
-    for (int E = 0; E <= 6; ++E) {
-        const int bits = top_bits - E;
-        const double bins = (double)(1 << bits);
-        const double scale = std::pow(10.0, -(double)E);
-        for (int f = 0; f < (1 << bits); ++f) {
-            const double mid = 0.1 + 0.9 * ((double)f + 0.5) / bins;
-            const float v = (float)(scale * mid);
-            out256[k++] = v;
-            if (is_signed) out256[k++] = -v;
-        }
-    }
-    if (k != 256) return fail(BITOPT_ERR_DEVICE, "bitopt_create_dynamic_map: internal count %d", k);
-    std::sort(out256, out256 + 256);
+    bitopt::build_dynamic_map(is_signed != 0, out256);
     return ok();
 }
 
@@ -180,7 +193,7 @@ int bitopt_quantize_blockwise(const void* x, int32_t dtype, int64_t n, const flo
     bitopt::CodecArgs a{};
     a.x = x; a.codes = codes; a.absmax = absmax; a.qmap = qmap; a.n = n;
     a.nb = (n + blocksize - 1) / blocksize;
-    a.vec = (aligned(x, 4 * elem_size(dtype)) && aligned(codes, 4)) ? 1 : 0;
+    a.vec = (aligned(x, 4 * elem_size(dtype)) && aligned(codes, 16)) ? 1 : 0;
     return device_status(bitopt::launch_quantize(a, dtype, blocksize, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 

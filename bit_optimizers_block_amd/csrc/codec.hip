@@ -5,7 +5,7 @@ namespace bitopt {
 
 template <int DT, int BS>
 static hipError_t quant_one(const CodecArgs& a, hipStream_t s) {
-    constexpr int64_t tile = (int64_t)TileChunks<BS>::v * 256;
+    constexpr int64_t tile = Layout<BS>::TE;
     hipLaunchKernelGGL((k_quantize<DT, BS>), tile_grid(a.n, tile), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

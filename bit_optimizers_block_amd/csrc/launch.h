@@ -17,11 +17,17 @@ hipError_t launch_step_lion(const StepArgs& a, int dtype, int bs, bool quant, bo
 hipError_t launch_quantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_dequantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 
-// Grid for a wave-per-tile kernel over n elements in tiles of `tile` elements.
+// Upper bound on resident-sized grids for the current device: compute units times
+// the groups per CU the step kernels are launched with (queried once per device).
+int64_t group_cap();
+
+// Grid for a wave-per-tile kernel over n elements in tiles of `tile` elements:
+// one tile per wave up to group_cap() groups, grid-stride beyond.
 inline dim3 tile_grid(int64_t n, int64_t tile) {
     const int64_t tiles = (n + tile - 1) / tile;
     int64_t groups = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    if (groups > (1 << 22)) groups = 1 << 22;   // grid-stride beyond this
+    const int64_t cap = group_cap();
+    if (groups > cap) groups = cap;
     if (groups < 1) groups = 1;
     return dim3((unsigned)groups);
 }
