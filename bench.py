@@ -12,8 +12,12 @@ position (algorithmic bytes / average launch time from HIP events on the launch
 stream) and the CPU oracle's throughput on a bounded sample of the same workload.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -79,49 +83,215 @@ class Replica:
         else:
             bitopt.step_8bit_blockwise_1state(hp, t, self.p, self.g, self.s1, self.a1, q1)
 
+    def raw_launcher(self, hp, q1, q2):
+        """The same call with its ctypes arguments built once (the timed loop's host
+        cost then stays far below a kernel's duration)."""
+        import ctypes
+        L = bitopt.lib()
+        h = bitopt.make_hparams(hp)
+        ptr = lambda x: ctypes.c_void_p(x.data_ptr())
+        dt = bitopt.DTYPES[self.p.dtype]
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if self.two:
+            f = L.bitopt_step_8bit_blockwise_2state
+            tail = (ptr(self.s1), ptr(self.s2), ptr(self.a1), ptr(self.a2), ptr(q1), ptr(q2), stream)
+        else:
+            f = L.bitopt_step_8bit_blockwise_1state
+            tail = (ptr(self.s1), ptr(self.a1), ptr(q1), stream)
+        head = (ctypes.byref(h), )
+        mid = (ptr(self.p), ptr(self.g), dt, self.n)
+        self._keep = h
+
+        def launch(t):
+            rc = f(*head, t, *mid, *tail)
+            if rc != 0:
+                raise bitopt.BitoptError(rc, bitopt.last_error())
+        return launch
+
 
 def cpu_baseline(wl, target_s=15.0):
-    """The oracle, as it stands, on a bounded sample of the same workload's blocks."""
+    """The oracle, as it stands, on a bounded sample of the same workload: a prefix
+    of the tensor (whole blocks) when one pass over all of it would exceed the
+    target time, else repeated full steps until about target_s seconds."""
     import oracle
     t = wl.tensors[0]
     hp = wl.hp
     B = hp["blocksize"]
     n_all = t.numel
     threads = oracle.get_threads()
+    k1 = 2 if hp["optimizer"] == "ademamix" else 1
+    two = hp["optimizer"] in ("adam", "adamw", "ademamix")
+    q1, q2 = oracle.dynamic_map(True), oracle.dynamic_map(False)
 
-    def run(nblocks):
-        n = min(n_all, nblocks * B)
+    def run(n, steps):
         p = W.to_dtype(W.normal_f32([wl.seed, 1, 0, 0], n_all, wl.p_scale, 0, n), t.dtype)
         g = W.to_dtype(W.normal_f32([wl.seed, 2, 0, 0], n_all, wl.g_scale, 0, n), t.dtype)
         nb = (n + B - 1) // B
-        k1 = 2 if hp["optimizer"] == "ademamix" else 1
-        two = hp["optimizer"] in ("adam", "adamw", "ademamix")
         s1, a1 = np.zeros(k1 * n, np.uint8), np.zeros(k1 * nb, np.float32)
         s2 = np.zeros(n, np.uint8) if two else None
         a2 = np.zeros(nb, np.float32) if two else None
-        q1, q2 = oracle.dynamic_map(True), oracle.dynamic_map(False)
         t0 = time.perf_counter()
-        oracle.step_8bit(hp, 1, p, g, t.dtype, s1, a1, q1, s2, a2, q2 if two else None)
-        return n, time.perf_counter() - t0
+        for step in range(1, steps + 1):
+            oracle.step_8bit(hp, step, p, g, t.dtype, s1, a1, q1, s2, a2, q2 if two else None)
+        return time.perf_counter() - t0
 
-    n, dt = run(max(1, 65536 // B))                     # calibration: 64K elements
-    want = int(n * target_s / max(dt, 1e-6))
-    n, dt = run(max(1, min(n_all, want) // B))
-    return {"value": n / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} elements ({(n + B - 1) // B} blocks of {B}) of the same workload, "
-                      f"1 step, {dt:.1f} s on {threads} threads"}
+    n0 = min(n_all, 256 * B)
+    dt0 = run(n0, 1)                                   # calibration
+    per_elem = dt0 / n0
+    if per_elem * n_all <= target_s:
+        n, steps = n_all, max(1, int(target_s / (per_elem * n_all)))
+    else:
+        n, steps = max(B, int(target_s / per_elem) // B * B), 1
+    dt = run(n, steps)
+    what = "the whole tensor" if n == n_all else f"the first {n} elements ({n // B} blocks of {B})"
+    return {"value": n * steps / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} of the same workload, {steps} step(s), {dt:.1f} s on {threads} threads"}
+
+
+def source_hash() -> str:
+    """Hash of the HIP library's sources: HBM traffic counted by the profiler is
+    reported only while the kernels are unchanged since the counters were taken."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_optimizers_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the step kernel from the committed counter summary,
+    or None if there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+COPY_ELEMS = 64 << 20          # calibration copy: 64 Mi fp32 = 256 MiB read + 256 MiB written
+
+
+def copy_calibration(dev):
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _rocprof(args, outdir, extra, env=None):
+    cmd = ["rocprofv3", *extra, "--output-format", "csv", "-d", outdir, "-o", "run", "--",
+           sys.executable, os.path.abspath(__file__), *args]
+    print("+ " + " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=300)
+    if r.returncode != 0:
+        raise SystemExit(f"rocprofv3 failed ({r.returncode}): {' '.join(cmd)}")
+    return " ".join(cmd)
+
+
+def _csv_rows(outdir, suffix):
+    rows = []
+    for f in glob.glob(os.path.join(outdir, "**", f"*{suffix}"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def profile(workload: str, outdir: str, steps: int):
+    """Kernel trace plus FETCH_SIZE and WRITE_SIZE passes (each its own run) of the
+    benchmark; writes <workload>.md and .json into outdir (the summaries kept under
+    profiles/ are these files)."""
+    env = dict(os.environ, TMPDIR="/tmp")
+    outdir = os.path.abspath(outdir)
+    base = ["--workload", workload, "--steps", str(steps), "--warmup", "3", "--no-cpu-baseline"]
+    cmds = {}
+    cmds["trace"] = _rocprof(base, os.path.join(outdir, "trace"), ["--kernel-trace", "--stats"], env)
+    cmds["fetch"] = _rocprof(base + ["--copy-calibration"], os.path.join(outdir, "fetch"), ["--pmc", "FETCH_SIZE"], env)
+    cmds["write"] = _rocprof(base + ["--copy-calibration"], os.path.join(outdir, "write"), ["--pmc", "WRITE_SIZE"], env)
+
+    stats = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")]
+    step_stats = [r for r in stats if "k_step" in r["Name"]]
+    kname = step_stats[0]["Name"]
+    avg_ns = float(step_stats[0]["AverageNs"])
+    calls = int(step_stats[0]["Calls"])
+
+    def counter(name, sub):
+        rows = [r for r in _csv_rows(os.path.join(outdir, sub), "counter_collection.csv") if r["Counter_Name"] == name]
+        step = [float(r["Counter_Value"]) for r in rows if "k_step" in r["Kernel_Name"]]
+        # the calibration copy is the runtime's device-to-device blit kernel: the
+        # dispatches of it with the largest grid
+        blits = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        gmax = max(int(r["Grid_Size"]) for r in blits)
+        copy = [float(r["Counter_Value"]) for r in blits if int(r["Grid_Size"]) == gmax]
+        return step, copy
+
+    fs, fc = counter("FETCH_SIZE", "fetch")
+    ws, wc = counter("WRITE_SIZE", "write")
+    # the timed launches are the last `steps` step-kernel dispatches of each run
+    fs, ws = fs[-steps:], ws[-steps:]
+    copy_kib = COPY_ELEMS * 4 / 1024.0
+    f_scale = copy_kib / (sum(fc) / len(fc))
+    w_scale = copy_kib / (sum(wc) / len(wc))
+    fetch_b = sum(fs) / len(fs) * f_scale * 1024.0
+    write_b = sum(ws) / len(ws) * w_scale * 1024.0
+    wl = workload_by_name(workload)
+    t = wl.tensors[0]
+    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1}[wl.hp["optimizer"]]
+    alg = W.bytes_per_element(t.dtype, ns, wl.hp["blocksize"]) * t.numel
+    d = {"workload": workload, "kernel": kname, "source_hash": source_hash(),
+         "kernel_trace_calls": calls, "kernel_trace_avg_us": avg_ns / 1e3,
+         "fetch_kib_per_launch": sum(fs) / len(fs), "write_kib_per_launch": sum(ws) / len(ws),
+         "copy_calibration": {"bytes_each_way": COPY_ELEMS * 4, "fetch_kib": sum(fc) / len(fc),
+                              "write_kib": sum(wc) / len(wc), "fetch_scale": f_scale, "write_scale": w_scale},
+         "traffic_bytes_per_launch": fetch_b + write_b, "algorithmic_bytes_per_launch": alg,
+         "commands": cmds}
+    with open(os.path.join(outdir, f"{workload}.json"), "w") as f:
+        json.dump(d, f, indent=1)
+    with open(os.path.join(outdir, f"{workload}.md"), "w") as f:
+        f.write(f"# {workload}: rocprofv3 summary\n\n")
+        f.write(f"Kernel: `{kname}`\n\n")
+        f.write("| figure | value |\n|---|---|\n")
+        f.write(f"| kernel-trace calls | {calls} |\n")
+        f.write(f"| kernel-trace average duration | {avg_ns / 1e3:.2f} us |\n")
+        f.write(f"| algorithmic bytes per launch | {alg / 1e6:.1f} MB |\n")
+        f.write(f"| algorithmic GB/s at the trace average | {alg / avg_ns:.0f} |\n")
+        f.write(f"| FETCH_SIZE per launch (raw) | {sum(fs) / len(fs):.0f} KiB |\n")
+        f.write(f"| WRITE_SIZE per launch (raw) | {sum(ws) / len(ws):.0f} KiB |\n")
+        f.write(f"| copy calibration (256 MiB each way): FETCH_SIZE / WRITE_SIZE | "
+                f"{sum(fc) / len(fc):.0f} / {sum(wc) / len(wc):.0f} KiB -> scale {f_scale:.4f} / {w_scale:.4f} |\n")
+        f.write(f"| HBM traffic per launch (scaled) | {(fetch_b + write_b) / 1e6:.1f} MB "
+                f"({(fetch_b + write_b) / alg:.3f} x algorithmic) |\n")
+        f.write(f"| library source hash | {source_hash()} |\n\n")
+        f.write("Commands (run from /tmp, TMPDIR=/tmp; raw output in the -d directories):\n\n")
+        for k, c in cmds.items():
+            f.write(f"- {k}: `{c}`\n")
+    print(json.dumps(d))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="adamw_fp32_b256")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 256 MiB with torch (profiler scale factor)")
+    ap.add_argument("--profile", metavar="OUTDIR",
+                    help="run the benchmark under rocprofv3 (kernel trace, FETCH_SIZE, WRITE_SIZE); "
+                         "raw output and the <workload>.md/.json summaries go to OUTDIR")
+    ap.add_argument("--profile-steps", type=int, default=20)
     args = ap.parse_args()
+    if args.profile:
+        profile(args.workload, args.profile, args.profile_steps)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the optimizer step is per-rank local (blocks are independent), "
               "and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
@@ -147,16 +317,31 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    launch = [r.raw_launcher(hp, q1, q2) for r in reps]
+    # timed region: K back-to-back launches between two events on the launch stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    ev[0].record(stream)
+    e0.record(stream)
+    h0 = time.perf_counter()
     for k in range(args.steps):
         step_no += 1
-        reps[k % len(reps)].step(hp, step_no, q1, q2)
-        ev[k + 1].record(stream)
+        launch[k % len(reps)](step_no)
+    host_us = (time.perf_counter() - h0) * 1e6 / args.steps
+    e1.record(stream)
     torch.cuda.synchronize()
-    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])   # ms
-    total_ms = ev[0].elapsed_time(ev[-1])
+    total_ms = e0.elapsed_time(e1)
+    # distribution of single launches (separate pass, an event pair around each)
+    nd = min(args.steps, 50)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nd)]
+    for k in range(nd):
+        step_no += 1
+        ev[2 * k].record(stream)
+        launch[k % len(reps)](step_no)
+        ev[2 * k + 1].record(stream)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(dev)
+    per = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(nd)])   # ms
     avg_ms = total_ms / args.steps
     value = n * args.steps / (total_ms / 1e3) / 1e9
     achieved = bpe * n / (avg_ms / 1e3) / 1e9
@@ -170,10 +355,11 @@ def main():
                    "param_dtype": t.dtype, "blocksize": B, "weight_decay": hp.get("weight_decay", 0.0),
                    "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(args.workload),
                      "bytes_per_elem": bpe, "kernel_ms_median": round(float(np.median(per)), 5),
                      "kernel_ms_p10": round(float(np.percentile(per, 10)), 5),
-                     "kernel_ms_p90": round(float(np.percentile(per, 90)), 5)},
+                     "kernel_ms_p90": round(float(np.percentile(per, 90)), 5),
+                     "host_us_per_launch": round(host_us, 2)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
