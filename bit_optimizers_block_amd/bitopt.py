@@ -64,6 +64,16 @@ def make_hparams(hp: dict) -> HParams:
     return h
 
 
+class Tensor(ctypes.Structure):
+    """Mirror of bitopt_tensor."""
+    _fields_ = [
+        ("p", ctypes.c_void_p), ("g", ctypes.c_void_p),
+        ("state1", ctypes.c_void_p), ("state2", ctypes.c_void_p),
+        ("absmax1", ctypes.c_void_p), ("absmax2", ctypes.c_void_p),
+        ("n", ctypes.c_int64), ("dtype", ctypes.c_int32), ("is_8bit", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -87,6 +97,8 @@ def lib():
             "bitopt_step_8bit_blockwise_1state": ([HP, i32, P, P, i32, i64, P, P, P, P], ctypes.c_int),
             "bitopt_step_32bit_2state": ([HP, i32, P, P, i32, i64, P, P, P], ctypes.c_int),
             "bitopt_step_32bit_1state": ([HP, i32, P, P, i32, i64, P, P], ctypes.c_int),
+            "bitopt_multi_workspace_bytes": ([i32], i64),
+            "bitopt_step_multi": ([HP, i32, ctypes.POINTER(Tensor), i32, P, P, P, i64, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -220,3 +232,44 @@ def step_32bit_1state(hp, step, p, g, state1, stream=None):
     _need(p, "p"); _need(g, "g", p.dtype, n); _need(state1, "state1", torch.float32, n)
     _check(lib().bitopt_step_32bit_1state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
                                           _ptr(state1), _stream(stream)))
+
+
+def multi_workspace_bytes(count: int) -> int:
+    return lib().bitopt_multi_workspace_bytes(int(count))
+
+
+def step_multi(hp, step, tensors, qmap1=None, qmap2=None, workspace=None, stream=None):
+    """One step over many tensors.  `tensors`: list of dicts with keys p, g, state1,
+    state2, absmax1, absmax2 (torch tensors or None) and is_8bit (bool).  Returns the
+    workspace tensor used (pass it back to reuse it)."""
+    h = make_hparams(hp)
+    two = h.optimizer in (OPTIMIZERS["adam"], OPTIMIZERS["ademamix"])
+    k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
+    arr = (Tensor * max(1, len(tensors)))()
+    dev = None
+    for i, t in enumerate(tensors):
+        p, g = t["p"], t["g"]
+        n = p.numel()
+        nb = nblocks(n, h.blocksize)
+        eight = bool(t.get("is_8bit", True))
+        _need(p, "p"); _need(g, "g", p.dtype, n)
+        sdt = torch.uint8 if eight else torch.float32
+        _need(t["state1"], "state1", sdt, k * n)
+        if two:
+            _need(t["state2"], "state2", sdt, n)
+        if eight:
+            _need(t["absmax1"], "absmax1", torch.float32, k * nb)
+            if two:
+                _need(t["absmax2"], "absmax2", torch.float32, nb)
+        arr[i] = Tensor(p.data_ptr(), g.data_ptr(), t["state1"].data_ptr(),
+                        t["state2"].data_ptr() if two else None,
+                        t["absmax1"].data_ptr() if eight else None,
+                        t["absmax2"].data_ptr() if (eight and two) else None,
+                        n, _dt(p), 1 if eight else 0)
+        dev = p.device
+    need = multi_workspace_bytes(len(tensors))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib().bitopt_step_multi(ctypes.byref(h), int(step), arr, len(tensors), _ptr(qmap1), _ptr(qmap2),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace

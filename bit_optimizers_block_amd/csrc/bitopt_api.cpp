@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "bitopt.h"
 #include "dynamic_map.h"
@@ -138,6 +139,17 @@ hipError_t dispatch_step(const bitopt::StepArgs& a, int opt, int dtype, int bs, 
     }
 }
 
+// Elements per wave tile of the step kernels (Layout<BS>::TE).
+int64_t tile_elems(int32_t blocksize) { return blocksize >= 1024 ? blocksize : 1024; }
+
+bool vec_ok(const bitopt_hparams* hp, const void* p, const void* g, int32_t dtype, int64_t n,
+            const void* s1, const void* s2) {
+    const int es = elem_size(dtype);
+    bool vec = aligned(p, 4 * es) && aligned(g, 4 * es) && aligned(s1, 16) && (!s2 || aligned(s2, 16));
+    if (hp->optimizer == BITOPT_ADEMAMIX) vec = vec && (n % 16 == 0);
+    return vec;
+}
+
 int run_step(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype, int64_t n,
              void* s1, void* s2, float* a1, float* a2, const float* q1, const float* q2, bool quant,
              void* stream, const char* fn) {
@@ -146,13 +158,7 @@ int run_step(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int
     a.n = n;
     a.nb = (n + hp->blocksize - 1) / hp->blocksize;
     a.s = make_scalars(*hp, step);
-    const int es = elem_size(dtype);
-    const bool ademamix = hp->optimizer == BITOPT_ADEMAMIX;
-    // Vector path: 4 parameters per access, codes in 16-byte words, fp32 states in
-    // 16-byte words; AdEMAMix's m2 starts n elements after m1.
-    bool vec = aligned(p, 4 * es) && aligned(g, 4 * es) && aligned(s1, 16) && (!s2 || aligned(s2, 16));
-    if (ademamix) vec = vec && (n % 16 == 0);
-    a.vec = vec ? 1 : 0;
+    a.vec = vec_ok(hp, p, g, dtype, n, s1, s2) ? 1 : 0;
     hipError_t e = dispatch_step(a, hp->optimizer, dtype, hp->blocksize, quant, hp->skip_zeros != 0,
                                  hp->max_unorm > 0.0f, reinterpret_cast<hipStream_t>(stream));
     return device_status(e, fn);
@@ -263,6 +269,86 @@ int bitopt_step_32bit_1state(const bitopt_hparams* hp, int32_t step, void* p, co
     if (n == 0) return ok();
     if (!p || !g || !state1) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     return run_step(hp, step, p, g, dtype, n, state1, nullptr, nullptr, nullptr, nullptr, nullptr, false, stream, fn);
+}
+
+int64_t bitopt_multi_workspace_bytes(int32_t count) {
+    if (count < 0) return -1;
+    return (int64_t)count * (int64_t)sizeof(bitopt::TensorDesc);
+}
+
+int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tensor* tensors, int32_t count,
+                      const float* qmap1, const float* qmap2, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+    const char* fn = "bitopt_step_multi";
+    if (int rc = check_hparams(hp, step, 0, fn)) return rc;
+    if (count < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: count < 0", fn);
+    if (count == 0) return ok();
+    if (!tensors) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensors is NULL", fn);
+    const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
+    bool any8 = false;
+    for (int32_t i = 0; i < count; ++i) {
+        const bitopt_tensor& t = tensors[i];
+        if (t.n < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: n < 0", fn, i);
+        if (!valid_dtype(t.dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: unknown dtype %d", fn, i, t.dtype);
+        if (t.n == 0) continue;
+        if (!t.p || !t.g || !t.state1 || (two && !t.state2))
+            return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: NULL pointer", fn, i);
+        if (t.is_8bit && (!t.absmax1 || (two && !t.absmax2)))
+            return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: NULL absmax", fn, i);
+        any8 = any8 || t.is_8bit;
+    }
+    if (any8 && (!qmap1 || (two && !qmap2))) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL qmap", fn);
+    if (!workspace || workspace_bytes < bitopt_multi_workspace_bytes(count) || !aligned(workspace, 16))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace missing, too small or not 16-byte aligned", fn);
+
+    // Group by kind (is_8bit, dtype), keeping call order inside a group; chunks of
+    // at most kMaxTableTensors tensors form one launch each.
+    const int64_t te = tile_elems(hp->blocksize);
+    struct Launch { int kind8, dtype; size_t first, count; int64_t tiles; };
+    std::vector<bitopt::TensorDesc> table;
+    std::vector<Launch> launches;
+    table.reserve((size_t)count);
+    for (int kind8 = 1; kind8 >= 0; --kind8) {
+        for (int dt = BITOPT_F32; dt <= BITOPT_BF16; ++dt) {
+            Launch L{kind8, dt, table.size(), 0, 0};
+            for (int32_t i = 0; i < count; ++i) {
+                const bitopt_tensor& t = tensors[i];
+                if (t.n == 0 || (t.is_8bit != 0) != (kind8 != 0) || t.dtype != dt) continue;
+                if (L.count == (size_t)bitopt::kMaxTableTensors) {
+                    launches.push_back(L);
+                    L = Launch{kind8, dt, table.size(), 0, 0};
+                }
+                bitopt::TensorDesc d{};
+                d.p = t.p; d.g = t.g; d.s1 = t.state1; d.s2 = two ? t.state2 : nullptr;
+                d.a1 = kind8 ? t.absmax1 : nullptr; d.a2 = (kind8 && two) ? t.absmax2 : nullptr;
+                d.n = t.n; d.nb = (t.n + hp->blocksize - 1) / hp->blocksize;
+                d.tile0 = L.tiles;
+                d.vec = vec_ok(hp, t.p, t.g, t.dtype, t.n, t.state1, two ? t.state2 : nullptr) ? 1 : 0;
+                L.tiles += (t.n + te - 1) / te;
+                ++L.count;
+                table.push_back(d);
+            }
+            if (L.count) launches.push_back(L);
+        }
+    }
+    if (table.empty()) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(workspace, table.data(), table.size() * sizeof(bitopt::TensorDesc),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return device_status(e, fn);
+    const bitopt::StepScalars sc = make_scalars(*hp, step);
+    for (const Launch& L : launches) {
+        bitopt::StepArgs a{};
+        a.q1 = qmap1; a.q2 = qmap2; a.s = sc;
+        a.table = reinterpret_cast<const bitopt::TensorDesc*>(workspace) + L.first;
+        a.ntab = (int32_t)L.count;
+        a.total_tiles = L.tiles;
+        a.n = 0; a.nb = 0; a.vec = 0;
+        e = dispatch_step(a, hp->optimizer, L.dtype, hp->blocksize, L.kind8 != 0, hp->skip_zeros != 0,
+                          hp->max_unorm > 0.0f, s);
+        if (e != hipSuccess) return device_status(e, fn);
+    }
+    return ok();
 }
 
 }  // extern "C"

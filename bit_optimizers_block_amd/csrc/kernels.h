@@ -40,6 +40,23 @@ struct StepScalars {
     float max_unorm;
 };
 
+// One tensor of a multi-tensor launch (device table entry): the same fields as a
+// single-tensor call plus the index of its first tile in the launch.
+struct TensorDesc {
+    void* p;
+    const void* g;
+    void* s1;
+    void* s2;
+    float* a1;
+    float* a2;
+    int64_t n;
+    int64_t nb;
+    int64_t tile0;
+    int32_t vec;
+    int32_t pad;
+};
+constexpr int kMaxTableTensors = 1024;     // tensors per multi-tensor launch
+
 struct StepArgs {
     void* p;
     const void* g;
@@ -53,6 +70,9 @@ struct StepArgs {
     int64_t nb;        // number of blocks
     int32_t vec;       // 1: every buffer is aligned for the vector path
     StepScalars s;
+    const TensorDesc* table;   // multi-tensor launch: ntab tensors (the fields above unused)
+    int32_t ntab;
+    int64_t total_tiles;
 };
 
 template <int OPT> struct NumStates { static constexpr int v = OPT == kAdemamix ? 3 : (OPT == kAdam ? 2 : 1); };
@@ -691,16 +711,30 @@ __device__ __forceinline__ int64_t wave_id() {
 // range on aligned buffers take the vector path, the ragged last tile (or every
 // tile of an unaligned call) the guarded path.
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool FAST>
-__device__ __forceinline__ void step_tiles(const StepArgs& a, const MapLDS& M1, const MapLDS& M2) {
+__device__ __forceinline__ void step_tiles(const StepArgs& a0, const MapLDS& M1, const MapLDS& M2,
+                                           const int64_t* T0) {
     using R = TileRaw<DT, OPT, BS, QUANT>;
     constexpr int64_t TE = Layout<BS>::TE;
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerGroup;
-    const int64_t ntiles = (a.n + TE - 1) / TE;
-    const int64_t nfull = a.vec ? a.n / TE : 0;
-    for (int64_t t = wave_id(); t < ntiles; t += stride) {
+    const int64_t ntiles = a0.table ? a0.total_tiles : (a0.n + TE - 1) / TE;
+    for (int64_t gt = wave_id(); gt < ntiles; gt += stride) {
+        StepArgs a = a0;
+        int64_t t = gt;
+        if (a0.table) {
+            // the tensor holding global tile gt: the last one whose first tile is <= gt
+            int lo = 0, hi = a0.ntab - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (T0[mid] <= gt) lo = mid; else hi = mid - 1;
+            }
+            const TensorDesc& d = a0.table[__builtin_amdgcn_readfirstlane(lo)];
+            a.p = d.p; a.g = d.g; a.s1 = d.s1; a.s2 = d.s2; a.a1 = d.a1; a.a2 = d.a2;
+            a.n = d.n; a.nb = d.nb; a.vec = d.vec;
+            t = gt - d.tile0;
+        }
         R x;
-        if (t < nfull) {
+        if (a.vec && (t + 1) * TE <= a.n) {
             load_tile<DT, OPT, BS, QUANT, true>(a, t * TE, lane, x);
             process_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST, true>(a, M1, M2, t * TE, lane, x);
         } else {
@@ -716,14 +750,19 @@ __global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
     __shared__ float Q1[256], Q2[256], T1[256], T2[256];
     __shared__ __attribute__((aligned(16))) uint8_t B1[search::kNB];
     __shared__ __attribute__((aligned(16))) uint8_t B2[search::kNB];
+    __shared__ int64_t T0[kMaxTableTensors];
     const MapLDS M1{Q1, T1, B1}, M2{Q2, T2, B2};
+    if (a.table) {
+        for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = a.table[i].tile0;
+        __syncthreads();
+    }
     if constexpr (QUANT) {
         if (stage_maps<NMAPS>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2))
-            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, true>(a, M1, M2);
+            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, true>(a, M1, M2, T0);
         else
-            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, false>(a, M1, M2);
+            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, false>(a, M1, M2, T0);
     } else {
-        step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, false>(a, M1, M2);
+        step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, false>(a, M1, M2, T0);
     }
 }
 

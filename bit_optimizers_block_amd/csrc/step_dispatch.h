@@ -10,7 +10,8 @@ namespace bitopt {
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM>
 hipError_t launch_one(const StepArgs& a, hipStream_t s) {
     constexpr int64_t tile = Layout<BS>::TE;
-    hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM>), tile_grid(a.n, tile), dim3(kThreads), 0, s, a);
+    const int64_t work = a.table ? a.total_tiles * tile : a.n;
+    hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM>), tile_grid(work, tile), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

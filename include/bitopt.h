@@ -189,6 +189,51 @@ BITOPT_API int bitopt_step_32bit_2state(const bitopt_hparams* hp, int32_t step, 
 BITOPT_API int bitopt_step_32bit_1state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
                              int32_t dtype, int64_t n, float* state1, void* stream);
 
+/*
+ * One tensor of a multi-tensor step (host-side descriptor; every pointer inside is
+ * caller-owned device memory):
+ *   p, g      n elements of dtype
+ *   state1    is_8bit: uint8 codes, n bytes (AdEMAMix 2n); else fp32 states, n (AdEMAMix 2n)
+ *   state2    2-state optimizers: uint8 codes / fp32 states, n; 1-state: NULL
+ *   absmax1   is_8bit: ceil(n/blocksize) fp32 (AdEMAMix 2x); else NULL
+ *   absmax2   is_8bit and 2-state: ceil(n/blocksize) fp32; else NULL
+ *   is_8bit   0 selects the 32-bit step, as for tensors below min_8bit_size
+ *             ("optim_overview": min_8bit_size, default 4096)
+ */
+typedef struct bitopt_tensor {
+    void* p;
+    const void* g;
+    void* state1;
+    void* state2;
+    float* absmax1;
+    float* absmax2;
+    int64_t n;
+    int32_t dtype;
+    int32_t is_8bit;
+} bitopt_tensor;
+
+/* Bytes of device workspace bitopt_step_multi needs for `count` tensors (< 0 if count < 0). */
+BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
+
+/*
+ * One optimizer step over many tensors: the same result, bit for bit, as calling
+ * the per-tensor 8-bit or 32-bit entry point (by is_8bit) on each tensor with the
+ * same hp and step.  Tensors are grouped by (dtype, is_8bit); each group is one
+ * kernel launch over all of its tiles, so hundreds of small tensors cost a few
+ * launches.  A device table of the group's tensors is written into `workspace`
+ * (device, at least bitopt_multi_workspace_bytes(count) bytes, 16-byte aligned) by
+ * an asynchronous copy on `stream`; the host array `tensors` may be reused as soon
+ * as the call returns.  Work on one workspace must stay in stream order.
+ *   tensors   host array of count descriptors (n == 0 entries are skipped)
+ *   qmap1/2   device codebooks as for the per-tensor calls (needed when any
+ *             tensor is 8-bit; qmap2 for 2-state optimizers)
+ * Errors: as the per-tensor calls, checked for every tensor before anything is
+ * enqueued; a workspace that is too small or misaligned gives INVALID_ARG.
+ */
+BITOPT_API int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tensor* tensors,
+                                 int32_t count, const float* qmap1, const float* qmap2, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

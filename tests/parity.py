@@ -139,3 +139,115 @@ class Quant8:
             cmp.values(to_host(d["a2"]), o["a2"], param_rtol(self.dtype), what + " absmax2", kind="a")
         cmp.values(as_f32(to_host(d["p"], self.dtype), self.dtype), as_f32(o["p"], self.dtype),
                    param_rtol(self.dtype), what + " p")
+
+
+class SampledTensor:
+    """Full-size 8-bit (or 32-bit) state of one tensor on the device; the oracle
+    follows a sample of its blocks, each block as a one-block tensor of its own
+    (blocks are independent, so this is the same computation)."""
+
+    def __init__(self, hp: dict, n: int, dtype: str, blocks, p0_full: np.ndarray, eight: bool = True):
+        self.hp = dict(hp)
+        self.n, self.dtype, self.eight = n, dtype, eight
+        B = hp["blocksize"]
+        self.B = B
+        self.nb = nb = (n + B - 1) // B
+        opt = hp["optimizer"]
+        self.k1 = 2 if opt == "ademamix" else 1
+        self.two = n_states(opt) >= 2
+        self.blocks = np.array(sorted(set(int(b) for b in blocks if 0 <= b < nb)), dtype=np.int64)
+        sd = torch.uint8 if eight else torch.float32
+        self.d = dict(p=to_dev(p0_full, dtype),
+                      s1=torch.zeros(self.k1 * n, dtype=sd, device="cuda"),
+                      s2=torch.zeros(n, dtype=sd, device="cuda") if self.two else None,
+                      a1=torch.zeros(self.k1 * nb, device="cuda") if eight else None,
+                      a2=torch.zeros(nb, device="cuda") if (eight and self.two) else None)
+        self.q = (oracle.dynamic_map(True), oracle.dynamic_map(False))
+        self.o = []
+        for b in self.blocks:
+            lo, hi = b * B, min(n, (b + 1) * B)
+            L = hi - lo
+            if eight:
+                st = dict(s1=np.zeros(self.k1 * L, np.uint8), a1=np.zeros(self.k1, np.float32),
+                          s2=np.zeros(L, np.uint8) if self.two else None,
+                          a2=np.zeros(1, np.float32) if self.two else None)
+            else:
+                st = dict(s1=np.zeros(self.k1 * L, np.float32), s2=np.zeros(L, np.float32) if self.two else None)
+            st["p"] = p0_full[lo:hi].copy()
+            st["lo"], st["hi"] = lo, hi
+            self.o.append(st)
+        idx = np.concatenate([np.arange(o["lo"], o["hi"]) for o in self.o]) if self.o else np.zeros(0, np.int64)
+        self.idx = torch.from_numpy(idx).cuda()
+        self.bidx = torch.from_numpy(self.blocks).cuda()
+
+    def desc(self, g_dev):
+        """This tensor as a multi-tensor descriptor."""
+        return dict(p=self.d["p"], g=g_dev, state1=self.d["s1"], state2=self.d["s2"],
+                    absmax1=self.d["a1"], absmax2=self.d["a2"], is_8bit=self.eight)
+
+    def step_gpu(self, t, g_dev):
+        d = self.d
+        if self.eight and self.two:
+            bitopt.step_8bit_blockwise_2state(self.hp, t, d["p"], g_dev, d["s1"], d["s2"], d["a1"], d["a2"],
+                                              *self.qdev())
+        elif self.eight:
+            bitopt.step_8bit_blockwise_1state(self.hp, t, d["p"], g_dev, d["s1"], d["a1"], self.qdev()[0])
+        elif self.two:
+            bitopt.step_32bit_2state(self.hp, t, d["p"], g_dev, d["s1"], d["s2"])
+        else:
+            bitopt.step_32bit_1state(self.hp, t, d["p"], g_dev, d["s1"])
+
+    _qd = None
+
+    @classmethod
+    def qdev(cls):
+        if cls._qd is None:
+            cls._qd = (bitopt.create_dynamic_map(True).cuda(), bitopt.create_dynamic_map(False).cuda())
+        return cls._qd
+
+    def step_oracle(self, t, g_full: np.ndarray):
+        q1, q2 = self.q
+        for st in self.o:
+            g = np.ascontiguousarray(g_full[st["lo"]:st["hi"]])
+            if self.eight:
+                oracle.step_8bit(self.hp, t, st["p"], g, self.dtype, st["s1"], st["a1"], q1,
+                                 st["s2"], st["a2"], q2 if self.two else None)
+            else:
+                oracle.step_32bit(self.hp, t, st["p"], g, self.dtype, st["s1"], st["s2"])
+
+    def compare(self, cmp: Compare, what=""):
+        torch.cuda.synchronize()
+        if not self.o:
+            return
+        d = self.d
+        n, nb = self.n, self.nb
+        p_g = to_host(d["p"][self.idx], self.dtype)
+        p_o = np.concatenate([st["p"] for st in self.o])
+        cmp.values(as_f32(p_g, self.dtype), as_f32(p_o, self.dtype), param_rtol(self.dtype), what + " p")
+        for k in range(self.k1):
+            s_g = to_host(d["s1"][self.idx + k * n])
+            s_o = np.concatenate([st["s1"][k * (st["hi"] - st["lo"]):(k + 1) * (st["hi"] - st["lo"])]
+                                  for st in self.o])
+            if self.eight:
+                cmp.codes(s_g, s_o, what + f" state1[{k}]")
+                a_g = to_host(d["a1"][self.bidx + k * nb])
+                a_o = np.array([st["a1"][k] for st in self.o], np.float32)
+                cmp.values(a_g, a_o, param_rtol(self.dtype), what + f" absmax1[{k}]", kind="a")
+            else:
+                cmp.values(s_g, s_o, 1e-6, what + " state1", kind="a")
+        if self.two:
+            s_g = to_host(d["s2"][self.idx])
+            s_o = np.concatenate([st["s2"] for st in self.o])
+            if self.eight:
+                cmp.codes(s_g, s_o, what + " state2")
+                a_g = to_host(d["a2"][self.bidx])
+                a_o = np.array([st["a2"][0] for st in self.o], np.float32)
+                cmp.values(a_g, a_o, param_rtol(self.dtype), what + " absmax2", kind="a")
+            else:
+                cmp.values(s_g, s_o, 1e-6, what + " state2", kind="a")
+
+
+def sample_blocks(nb: int, k: int, seed: int, extra=()):
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(nb, size=min(k, nb), replace=False)
+    return np.unique(np.concatenate([pick, [0, nb - 1], np.asarray(extra, np.int64)]))

@@ -125,3 +125,31 @@ def test_binding_refuses_host_tensors(B):
     with pytest.raises(ValueError):
         B.step_8bit_blockwise_1state(dict(optimizer="lion"), 1, p, p, torch.zeros(16, dtype=torch.uint8),
                                      torch.zeros(1), torch.zeros(256))
+
+
+def test_multi_argument_errors(B):
+    L = B.lib()
+    E = B.ERR_INVALID_ARG
+    h = B.make_hparams(dict(optimizer="adam"))
+    P = ctypes.c_void_p(16)
+    assert L.bitopt_multi_workspace_bytes(146) == 146 * 80
+    assert L.bitopt_multi_workspace_bytes(-1) < 0
+    arr = (B.Tensor * 2)()
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 0, P, P, P, 0, None) == B.OK        # empty
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, -1, P, P, P, 0, None) == E
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, None, 2, P, P, P, 1000, None) == E
+    arr[0] = B.Tensor(16, 16, 16, 16, 16, 16, 100, 0, 1)
+    arr[1] = B.Tensor(16, 16, 16, None, 16, 16, 100, 0, 1)                                  # no state2
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, P, P, P, 1000, None) == E and "tensor 1" in B.last_error()
+    arr[1] = B.Tensor(16, 16, 16, 16, 16, None, 100, 0, 1)                                  # no absmax2
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, P, P, P, 1000, None) == E
+    arr[1] = B.Tensor(16, 16, 16, 16, None, None, 100, 0, 0)                                # 32-bit: fine
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, P, P, P, 10, None) == E and "workspace" in B.last_error()
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, P, P, ctypes.c_void_p(24), 1000, None) == E  # misaligned
+    arr[1] = B.Tensor(16, 16, 16, 16, None, None, 100, 5, 0)                                # bad dtype
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, P, P, P, 1000, None) == E and "dtype" in B.last_error()
+    arr[1] = B.Tensor(16, 16, 16, 16, None, None, -3, 0, 0)
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, P, P, P, 1000, None) == E
+    arr[0] = B.Tensor(16, 16, 16, 16, 16, 16, 0, 0, 1)                                      # n == 0 entries skipped
+    arr[1] = B.Tensor(None, None, None, None, None, None, 0, 0, 1)
+    assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, None, None, P, 1000, None) == B.OK
