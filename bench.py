@@ -48,8 +48,71 @@ def workload_by_name(name):
         "lion_fp16_skip0": lambda: W.c4_embedding("lion", False),
         "lion_fp16_skip1": lambda: W.c4_embedding("lion", True),
         "adam_fp32_256x256": W.c1_adam_256,
+        "gpt_1p3b": W.c5_gpt_1p3b,
     }
     return table[name]()
+
+
+def workload_bytes(wl) -> float:
+    """Algorithmic HBM bytes of one step over every tensor of the workload."""
+    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1}[wl.hp["optimizer"]]
+    total = 0.0
+    for t in wl.tensors:
+        if t.eightbit:
+            total += W.bytes_per_element(t.dtype, ns, wl.hp["blocksize"]) * t.numel
+        else:   # 32-bit states: read+write p, read g, read+write each fp32 state
+            ps = {"f32": 4, "f16": 2, "bf16": 2}[t.dtype]
+            total += (3 * ps + ns * 8) * t.numel
+    return total
+
+
+class Model:
+    """Device buffers of every tensor of a multi-tensor workload, stepped with one
+    bitopt_step_multi call (one launch per tensor kind)."""
+
+    def __init__(self, wl, dev):
+        import ctypes
+        hp = wl.hp
+        B = hp["blocksize"]
+        two = hp["optimizer"] in ("adam", "adamw", "ademamix")
+        k1 = 2 if hp["optimizer"] == "ademamix" else 1
+        self.bufs = []
+        arr = (bitopt.Tensor * len(wl.tensors))()
+        for i, t in enumerate(wl.tensors):
+            n = t.numel
+            nb = (n + B - 1) // B
+            dt = TORCH_DT[t.dtype]
+            p = torch.from_numpy(W.normal_f32([wl.seed, 1, i], n, wl.p_scale)).to(dev).to(dt)
+            g = torch.from_numpy(W.normal_f32([wl.seed, 2, i, 1], n, wl.g_scale)).to(dev).to(dt)
+            sd = torch.uint8 if t.eightbit else torch.float32
+            s1 = torch.zeros(k1 * n, dtype=sd, device=dev)
+            s2 = torch.zeros(n, dtype=sd, device=dev) if two else None
+            a1 = torch.zeros(k1 * nb, device=dev) if t.eightbit else None
+            a2 = torch.zeros(nb, device=dev) if (t.eightbit and two) else None
+            self.bufs.append((p, g, s1, s2, a1, a2))
+            ptr = lambda x: None if x is None else x.data_ptr()
+            arr[i] = bitopt.Tensor(p.data_ptr(), g.data_ptr(), s1.data_ptr(), ptr(s2), ptr(a1), ptr(a2), n,
+                                   bitopt.DTYPES[dt], 1 if t.eightbit else 0)
+        self.arr = arr
+        self.count = len(wl.tensors)
+        self.ws = torch.empty(bitopt.multi_workspace_bytes(self.count), dtype=torch.uint8, device=dev)
+        self.n = sum(t.numel for t in wl.tensors)
+
+    def launcher(self, hp, q1, q2):
+        import ctypes
+        L = bitopt.lib()
+        h = bitopt.make_hparams(hp)
+        self._keep = h
+        f = L.bitopt_step_multi
+        args = (ctypes.c_void_p(q1.data_ptr()), ctypes.c_void_p(q2.data_ptr()),
+                ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+        def launch(t):
+            rc = f(ctypes.byref(h), t, self.arr, self.count, *args)
+            if rc != 0:
+                raise bitopt.BitoptError(rc, bitopt.last_error())
+        return launch
 
 
 class Replica:
@@ -299,25 +362,46 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = workload_by_name(args.workload)
-    t = wl.tensors[0]
     hp = dict(wl.hp)
-    n = t.numel
     B = hp["blocksize"]
-    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1}[hp["optimizer"]]
-    bpe = W.bytes_per_element(t.dtype, ns, B)
+    multi = len(wl.tensors) > 1
     q1 = bitopt.create_dynamic_map(True).to(dev)
     q2 = bitopt.create_dynamic_map(False).to(dev)
-    reps = [Replica(wl, r, dev) for r in range(args.replicas)]
+    if multi:
+        model = Model(wl, dev)
+        n = model.n
+        step_bytes = workload_bytes(wl)
+        launchers = [model.launcher(hp, q1, q2)]
+    else:
+        t = wl.tensors[0]
+        n = t.numel
+        step_bytes = workload_bytes(wl)
+        reps = [Replica(wl, r, dev) for r in range(args.replicas)]
+        launchers = None
+        if hp.get("skip_zeros"):
+            # a block whose gradients are all zero needs only its gradient read
+            g = reps[0].g.float()
+            nbk = (n + B - 1) // B
+            pad = torch.zeros(nbk * B, device=dev)
+            pad[:n] = g.abs()
+            live = int((pad.view(nbk, B).amax(1) > 0).sum().item())
+            gsz = {"f32": 4, "f16": 2, "bf16": 2}[t.dtype]
+            step_bytes = step_bytes * live / nbk + gsz * B * (nbk - live)
     torch.cuda.synchronize()
 
     step_no = 0
-    for i in range(args.warmup):
-        step_no += 1
-        reps[i % len(reps)].step(hp, step_no, q1, q2)
+    if multi:
+        for i in range(args.warmup):
+            step_no += 1
+            launchers[0](step_no)
+    else:
+        for i in range(args.warmup):
+            step_no += 1
+            reps[i % len(reps)].step(hp, step_no, q1, q2)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    launch = [r.raw_launcher(hp, q1, q2) for r in reps]
+    launch = launchers if multi else [r.raw_launcher(hp, q1, q2) for r in reps]
     # timed region: K back-to-back launches between two events on the launch stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -325,7 +409,7 @@ def main():
     h0 = time.perf_counter()
     for k in range(args.steps):
         step_no += 1
-        launch[k % len(reps)](step_no)
+        launch[k % len(launch)](step_no)
     host_us = (time.perf_counter() - h0) * 1e6 / args.steps
     e1.record(stream)
     torch.cuda.synchronize()
@@ -336,7 +420,7 @@ def main():
     for k in range(nd):
         step_no += 1
         ev[2 * k].record(stream)
-        launch[k % len(reps)](step_no)
+        launch[k % len(launch)](step_no)
         ev[2 * k + 1].record(stream)
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -344,25 +428,33 @@ def main():
     per = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(nd)])   # ms
     avg_ms = total_ms / args.steps
     value = n * args.steps / (total_ms / 1e3) / 1e9
-    achieved = bpe * n / (avg_ms / 1e3) / 1e9
+    achieved = step_bytes / (avg_ms / 1e3) / 1e9
 
+    if multi:
+        cfg = {"workload": wl.name, "optimizer": hp["optimizer"], "tensors": len(wl.tensors),
+               "params": n, "eightbit_params": sum(t.numel for t in wl.tensors if t.eightbit),
+               "param_dtype": "bf16 (8-bit states), f32 (32-bit states)", "blocksize": B,
+               "launches_per_step": 2}
+    else:
+        cfg = {"workload": wl.name, "optimizer": hp["optimizer"], "shape": list(t.shape),
+               "param_dtype": t.dtype, "blocksize": B, "weight_decay": hp.get("weight_decay", 0.0),
+               "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps)}
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gelem/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(avg_ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "optimizer": hp["optimizer"], "shape": list(t.shape),
-                   "param_dtype": t.dtype, "blocksize": B, "weight_decay": hp.get("weight_decay", 0.0),
-                   "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps)},
+        "config": cfg,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(args.workload),
-                     "bytes_per_elem": bpe, "kernel_ms_median": round(float(np.median(per)), 5),
+                     "algorithmic_bytes_per_step": step_bytes,
+                     "kernel_ms_median": round(float(np.median(per)), 5),
                      "kernel_ms_p10": round(float(np.percentile(per, 10)), 5),
                      "kernel_ms_p90": round(float(np.percentile(per, 90)), 5),
                      "host_us_per_launch": round(host_us, 2)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not multi:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

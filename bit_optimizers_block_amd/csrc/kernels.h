@@ -103,18 +103,26 @@ template <> struct Elem<kF32>  { using T = float;    using Raw4 = u32x4; };
 template <> struct Elem<kF16>  { using T = uint16_t; using Raw4 = u32x2; };
 template <> struct Elem<kBF16> { using T = uint16_t; using Raw4 = u32x2; };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
-__device__ __forceinline__ uint32_t f32_to_half_bits(float f) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32, round to nearest even
-}
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+// fp32 -> fp16 / bf16, round to nearest even (v_cvt_f16_f32 / v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f32_to_half_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;   // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                               // nearest even
-    return u >> 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two values packed into one 32-bit word (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+template <int DT> __device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    if constexpr (DT == kF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <int DT> __device__ __forceinline__ float widen(uint32_t bits) {
@@ -147,8 +155,8 @@ template <int DT> __device__ __forceinline__ void store4(void* base, int64_t e, 
         r.x = __float_as_uint(v[0]); r.y = __float_as_uint(v[1]);
         r.z = __float_as_uint(v[2]); r.w = __float_as_uint(v[3]);
     } else {
-        r.x = narrow<DT>(v[0]) | (narrow<DT>(v[1]) << 16);
-        r.y = narrow<DT>(v[2]) | (narrow<DT>(v[3]) << 16);
+        r.x = narrow2<DT>(v[0], v[1]);
+        r.y = narrow2<DT>(v[2], v[3]);
     }
     st_stream(r, reinterpret_cast<Raw4*>(reinterpret_cast<typename Elem<DT>::T*>(base) + e));
 }
