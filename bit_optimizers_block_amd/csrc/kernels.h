@@ -7,12 +7,14 @@
 // 16-bit, 4 B/lane of codes) and carries the non-temporal hint.  Blocks of 256 are
 // single quads (four per tile): their absmax comes from one reduce-scatter across
 // the wave; a block of 2048 is a whole tile, reduced by DPP row shifts, row
-// broadcasts and readlane.  Tiles are software-pipelined two deep.  The 256-entry
-// codebooks sit in LDS; decoding is one LDS gather.  Encoding with a standard
-// dynamic map is one bucket lookup (exponent and top mantissa bits of x) plus one
-// comparison with an fp32 decision threshold, both in LDS; any other map falls
-// back to a branch-free binary search plus one neighbour comparison.  Both give
-// the nearest entry (fp32 distance, ties to the lower index).
+// broadcasts and readlane.  Full tiles keep the whole tile in registers and read
+// each input once; a ragged last tile (or any tile of a misaligned tensor) takes a
+// two-pass path that holds one quad at a time.  The 256-entry codebooks sit in
+// LDS; decoding is one LDS gather.  Encoding with a standard dynamic map is one
+// bucket lookup (exponent and top mantissa bits of x) plus one comparison with an
+// fp32 decision threshold, both in LDS; any other map falls back to a branch-free
+// binary search plus one neighbour comparison.  Both give the nearest entry (fp32
+// distance, ties to the lower index).
 //
 // Arithmetic.  Each element operation is one IEEE fp32 operation in a fixed order
 // (the build disables FMA contraction and keeps correctly rounded division and
@@ -89,13 +91,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef BITOPT_NONTEMPORAL
 #define BITOPT_NONTEMPORAL 1
 #endif
+
+// Every tensor the kernels touch lives in device (global) memory.  Pointers read from
+// the multi-tensor descriptor table would otherwise be generic, and generic (flat)
+// accesses share the LDS wait counter, so each LDS wait would also wait for every
+// outstanding HBM load.  Accesses go through gbl() so they compile to global ones.
+#define BITOPT_GLOBAL __attribute__((address_space(1)))
+template <class T> __device__ __forceinline__ BITOPT_GLOBAL T* gbl(T* p) { return (BITOPT_GLOBAL T*)p; }
+
 template <class T> __device__ __forceinline__ T ld_stream(const T* p) {
-    if constexpr (BITOPT_NONTEMPORAL) return __builtin_nontemporal_load(p);
-    else return *p;
+    if constexpr (BITOPT_NONTEMPORAL) return __builtin_nontemporal_load(gbl(p));
+    else return *gbl(p);
 }
 template <class T> __device__ __forceinline__ void st_stream(T v, T* p) {
-    if constexpr (BITOPT_NONTEMPORAL) __builtin_nontemporal_store(v, p);
-    else *p = v;
+    if constexpr (BITOPT_NONTEMPORAL) __builtin_nontemporal_store(v, gbl(p));
+    else *gbl(p) = v;
 }
 
 template <int DT> struct Elem;
@@ -162,13 +172,13 @@ template <int DT> __device__ __forceinline__ void store4(void* base, int64_t e, 
 }
 // Guarded element access (tail tiles and unaligned buffers).
 template <int DT> __device__ __forceinline__ float load1(const void* base, int64_t e) {
-    const typename Elem<DT>::T x = reinterpret_cast<const typename Elem<DT>::T*>(base)[e];
+    const typename Elem<DT>::T x = gbl(reinterpret_cast<const typename Elem<DT>::T*>(base))[e];
     if constexpr (DT == kF32) return x;
     else return widen<DT>((uint32_t)x);
 }
 template <int DT> __device__ __forceinline__ void store1(void* base, int64_t e, float v) {
-    if constexpr (DT == kF32) reinterpret_cast<float*>(base)[e] = v;
-    else reinterpret_cast<uint16_t*>(base)[e] = (uint16_t)narrow<DT>(v);
+    if constexpr (DT == kF32) gbl(reinterpret_cast<float*>(base))[e] = v;
+    else gbl(reinterpret_cast<uint16_t*>(base))[e] = (uint16_t)narrow<DT>(v);
 }
 
 // ---------------------------------------------------------------- wave reductions
@@ -258,41 +268,76 @@ __device__ __forceinline__ uint32_t encode(const MapLDS& m, float x) {
     }
 }
 
-// Stage up to two codebooks into LDS.  Every thread of the (256-thread) group
-// copies one entry and checks it against the two standard maps; the group takes
-// the table path only when every staged map is a standard one.  Returns that
-// choice (uniform over the group).
+// Stage up to two codebooks into LDS.  Map 1 is expected to be the standard signed
+// map and map 2 the standard unsigned one, so their search tables are fetched
+// together with the maps (one round of loads, one barrier).  Each wave votes on
+// which standard map each staged map equals; if the group's vote shows the
+// standard maps in the other assignment, the tables are staged again.  Returns
+// whether the table encoder applies (uniform over the group); otherwise the
+// caller uses the binary search over the staged maps.
 template <int NMAPS>
 __device__ __forceinline__ bool stage_maps(const float* q1, const float* q2, float* Q1, float* Q2,
-                                           float* T1, float* T2, uint8_t* B1, uint8_t* B2) {
+                                           float* T1, float* T2, uint8_t* B1, uint8_t* B2, uint32_t* vote) {
+    constexpr int NV = search::kNB / 16;                 // 16-byte words per bucket table
+    static_assert(search::kNB % 16 == 0 && NV <= 2 * kThreads, "bucket table staging");
     const int tid = threadIdx.x;
-    const float* src[2] = {q1, q2};
-    float* Q[2] = {Q1, Q2};
+    const u32x4* bs = reinterpret_cast<const u32x4*>(kStdBucket0);
+    const u32x4* bu = reinterpret_cast<const u32x4*>(kStdBucket1);
+    const bool two = tid + kThreads < NV;
+    // every load first
+    const uint32_t v1 = __float_as_uint(gbl(q1)[tid]);
+    const uint32_t v2 = NMAPS > 1 ? __float_as_uint(gbl(q2)[tid]) : 0u;
+    const uint32_t s0 = kStdQ0[tid], s1 = kStdQ1[tid];
+    const uint32_t t1 = kStdTau0[tid];
+    const uint32_t t2 = NMAPS > 1 ? kStdTau1[tid] : 0u;
+    const u32x4 b1a = bs[tid];
+    const u32x4 b1b = two ? bs[tid + kThreads] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 b2a = {0u, 0u, 0u, 0u}, b2b = {0u, 0u, 0u, 0u};
+    if constexpr (NMAPS > 1) {
+        b2a = bu[tid];
+        if (two) b2b = bu[tid + kThreads];
+    }
+    Q1[tid] = __uint_as_float(v1);
+    T1[tid] = __uint_as_float(t1);
+    reinterpret_cast<u32x4*>(B1)[tid] = b1a;
+    if (two) reinterpret_cast<u32x4*>(B1)[tid + kThreads] = b1b;
+    if constexpr (NMAPS > 1) {
+        Q2[tid] = __uint_as_float(v2);
+        T2[tid] = __uint_as_float(t2);
+        reinterpret_cast<u32x4*>(B2)[tid] = b2a;
+        if (two) reinterpret_cast<u32x4*>(B2)[tid + kThreads] = b2b;
+    }
+    // bit 0/1: map 1 equals the standard signed/unsigned map; bits 2/3: the same for map 2
+    uint32_t bits = 0;
+    if (__ballot(v1 != s0) == 0ull) bits |= 1u;
+    if (__ballot(v1 != s1) == 0ull) bits |= 2u;
+    if constexpr (NMAPS > 1) {
+        if (__ballot(v2 != s0) == 0ull) bits |= 4u;
+        if (__ballot(v2 != s1) == 0ull) bits |= 8u;
+    }
+    if ((tid & 63) == 0) vote[tid >> 6] = bits;
+    __syncthreads();
+    uint32_t all = vote[0];
+#pragma unroll
+    for (int w = 1; w < kWavesPerGroup; ++w) all &= vote[w];
+    if ((all & 1u) && (NMAPS == 1 || (all & 8u))) return true;
+    const int w1 = (all & 1u) ? 0 : (all & 2u) ? 1 : -1;
+    const int w2 = NMAPS == 1 ? 0 : (all & 4u) ? 0 : (all & 8u) ? 1 : -1;
+    if (w1 < 0 || w2 < 0) return false;
+    // standard maps in the other assignment (nothing has read the tables yet)
+    const int which[2] = {w1, w2};
     float* T[2] = {T1, T2};
     uint8_t* Bk[2] = {B1, B2};
-    int which[2] = {-1, -1};
 #pragma unroll
     for (int k = 0; k < NMAPS; ++k) {
-        const uint32_t v = __float_as_uint(src[k][tid]);
-        Q[k][tid] = __uint_as_float(v);
-        if (__syncthreads_and(v == kStdQ0[tid])) which[k] = 0;
-        else if (__syncthreads_and(v == kStdQ1[tid])) which[k] = 1;
-    }
-    bool fast = true;
-#pragma unroll
-    for (int k = 0; k < NMAPS; ++k) fast = fast && which[k] >= 0;
-    if (fast) {
-#pragma unroll
-        for (int k = 0; k < NMAPS; ++k) {
-            const uint32_t* tsrc = which[k] ? kStdTau1 : kStdTau0;
-            const uint32_t* bsrc = reinterpret_cast<const uint32_t*>(which[k] ? kStdBucket1 : kStdBucket0);
-            T[k][tid] = __uint_as_float(tsrc[tid]);
-            uint32_t* bdst = reinterpret_cast<uint32_t*>(Bk[k]);
-            for (int i = tid; i < search::kNB / 4; i += kThreads) bdst[i] = bsrc[i];
-        }
+        const uint32_t* tsrc = which[k] ? kStdTau1 : kStdTau0;
+        const u32x4* bsrc = which[k] ? bu : bs;
+        T[k][tid] = __uint_as_float(tsrc[tid]);
+        reinterpret_cast<u32x4*>(Bk[k])[tid] = bsrc[tid];
+        if (two) reinterpret_cast<u32x4*>(Bk[k])[tid + kThreads] = bsrc[tid + kThreads];
     }
     __syncthreads();
-    return fast;
+    return true;
 }
 
 // ---------------------------------------------------------------- optimizer updates
@@ -374,16 +419,15 @@ template <int BS> struct Layout {
 };
 
 // Block absmax and its reciprocal for the BPT blocks of a tile, from each lane's
-// partial maxima m[b] (non-negative).  Results are wave-uniform.
+// partial maxima m[b] (non-negative), left in lanes: with one block per tile every
+// lane holds the pair; with four, row b (lanes 16b .. 16b+15) holds block b's.
 // One block per tile: a wave max.  Four blocks per tile: a reduce-scatter -- two
 // exchanges between lane halves and row pairs leave row r with the partial max of
-// block r, a row reduction completes it, one reciprocal serves all four blocks, and
-// each block's pair is then read from its row's first lane.
+// block r, a row reduction completes it, and one reciprocal serves all four blocks.
 template <int BPT>
-__device__ __forceinline__ void block_absmax(const float (&m)[BPT], float (&A)[BPT], float (&r)[BPT]) {
+__device__ __forceinline__ void block_absmax_lanes(const float (&m)[BPT], float& u, float& ru) {
     if constexpr (BPT == 1) {
-        A[0] = wave_max_nonneg(m[0]);
-        r[0] = (A[0] == 0.0f) ? 0.0f : 1.0f / A[0];
+        u = wave_max_nonneg(m[0]);
     } else {
         static_assert(BPT == 4, "tiles hold one or four blocks");
         const int lane = threadIdx.x & 63;
@@ -396,31 +440,27 @@ __device__ __forceinline__ void block_absmax(const float (&m)[BPT], float (&A)[B
         const float w1 = fmaxf(k1, __shfl_xor(s1, 32, 64));
         // even rows keep the first of the pair, odd rows the second: row r -> block r
         const float s = odd ? w0 : w1, k = odd ? w1 : w0;
-        const float u = row_max_nonneg(fmaxf(k, __shfl_xor(s, 16, 64)));
-        const float ru = (u == 0.0f) ? 0.0f : 1.0f / u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            A[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), 16 * b));
-            r[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ru), 16 * b));
-        }
+        u = row_max_nonneg(fmaxf(k, __shfl_xor(s, 16, 64)));
     }
+    ru = (u == 0.0f) ? 0.0f : 1.0f / u;
 }
 
-// The NQ code words (4 codes each) of a lane from a code array.
-template <int BS, bool FULL>
-__device__ __forceinline__ void load_codes(const uint8_t* cp, int64_t base, int lane, int64_t n, uint32_t w[]) {
-    using L = Layout<BS>;
+// Block b's value of a pair left in lanes by block_absmax_lanes (wave-uniform).
+template <int BPT>
+__device__ __forceinline__ float block_value(float v, int b) {
+    if constexpr (BPT == 1) return v;
+    else return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * b));
+}
+
+// The same as uniform per-block values.
+template <int BPT>
+__device__ __forceinline__ void block_absmax(const float (&m)[BPT], float (&A)[BPT], float (&r)[BPT]) {
+    float u, ru;
+    block_absmax_lanes<BPT>(m, u, ru);
 #pragma unroll
-    for (int q = 0; q < L::NQ; ++q) {
-        const int64_t e = L::elem(base, lane, q);
-        if constexpr (FULL) {
-            w[q] = ld_stream(reinterpret_cast<const uint32_t*>(cp + e));
-        } else {
-            uint32_t x = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x |= (e + i < n ? (uint32_t)cp[e + i] : 0u) << (8 * i);
-            w[q] = x;
-        }
+    for (int b = 0; b < BPT; ++b) {
+        A[b] = block_value<BPT>(u, b);
+        r[b] = block_value<BPT>(ru, b);
     }
 }
 
@@ -431,7 +471,7 @@ __device__ __forceinline__ void store_code_word(uint8_t* cp, int64_t e, int64_t 
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (e + i < n) cp[e + i] = (uint8_t)(w >> (8 * i));
+            if (e + i < n) gbl(cp)[e + i] = (uint8_t)(w >> (8 * i));
     }
 }
 
@@ -467,8 +507,8 @@ __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ
 
 // ---------------------------------------------------------------- fused step tile
 
-// Raw inputs of one lane for one tile, as loaded: parameter and gradient words,
-// code words (8-bit) or fp32 states, and the tile's block absmax per state.
+// Raw inputs of one lane for one full tile, as loaded: parameter and gradient
+// words, code words (8-bit) or fp32 states, and the tile's block absmax per state.
 template <int DT, int OPT, int BS, bool QUANT>
 struct TileRaw {
     static constexpr int NQ = Layout<BS>::NQ;
@@ -482,23 +522,6 @@ struct TileRaw {
 };
 
 template <int DT, int PW>
-__device__ __forceinline__ void load_words(const void* base, int64_t e, int64_t n, uint32_t (&w)[PW]) {
-    if constexpr (DT == kF32) {
-        const float* f = reinterpret_cast<const float*>(base);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = e + i < n ? __float_as_uint(f[e + i]) : 0u;
-    } else {
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(base);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t lo = e + 2 * i < n ? (uint32_t)h[e + 2 * i] : 0u;
-            const uint32_t hi = e + 2 * i + 1 < n ? (uint32_t)h[e + 2 * i + 1] : 0u;
-            w[i] = lo | (hi << 16);
-        }
-    }
-}
-
-template <int DT, int PW>
 __device__ __forceinline__ void widen_words(const uint32_t (&w)[PW], float v[4]) {
     if constexpr (DT == kF32) {
 #pragma unroll
@@ -509,58 +532,54 @@ __device__ __forceinline__ void widen_words(const uint32_t (&w)[PW], float v[4])
     }
 }
 
-// Issue every load of one tile.  FULL: vector accesses (tile in range, buffers
-// aligned); otherwise element-wise guarded accesses, out-of-range values zero.
-template <int DT, int OPT, int BS, bool QUANT, bool FULL>
+// A full tile: in range, every buffer aligned for the vector path.
+template <int BS>
+__device__ __forceinline__ bool tile_full(const StepArgs& a, int64_t t) {
+    return a.vec && (t + 1) * Layout<BS>::TE <= a.n;
+}
+
+// Issue every load of one full tile (vector accesses).
+template <int DT, int OPT, int BS, bool QUANT>
 __device__ __forceinline__ void load_tile(const StepArgs& a, int64_t base, int lane,
                                           TileRaw<DT, OPT, BS, QUANT>& r) {
     using L = Layout<BS>;
     using R = TileRaw<DT, OPT, BS, QUANT>;
-    const int64_t n = a.n;
+    using Raw4 = typename Elem<DT>::Raw4;
+    using T = typename Elem<DT>::T;
     const int64_t blk0 = base / BS;
 #pragma unroll
     for (int q = 0; q < R::NQ; ++q) {
         const int64_t e = L::elem(base, lane, q);
-        if constexpr (FULL) {
-            using Raw4 = typename Elem<DT>::Raw4;
-            const Raw4 pv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const typename Elem<DT>::T*>(a.p) + e));
-            const Raw4 gv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const typename Elem<DT>::T*>(a.g) + e));
+        const Raw4 pv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const T*>(a.p) + e));
+        const Raw4 gv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const T*>(a.g) + e));
 #pragma unroll
-            for (int i = 0; i < R::PW; ++i) { r.p[q][i] = pv[i]; r.g[q][i] = gv[i]; }
-        } else {
-            load_words<DT, R::PW>(a.p, e, n, r.p[q]);
-            load_words<DT, R::PW>(a.g, e, n, r.g[q]);
-        }
+        for (int i = 0; i < R::PW; ++i) { r.p[q][i] = pv[i]; r.g[q][i] = gv[i]; }
     }
 #pragma unroll
     for (int k = 0; k < R::NS; ++k) {
         const int slot = Slot<OPT>::which(k);
-        const int64_t eo = Slot<OPT>::elem_off(k, n);
+        const int64_t eo = Slot<OPT>::elem_off(k, a.n);
         if constexpr (QUANT) {
-            load_codes<BS, FULL>(reinterpret_cast<const uint8_t*>(slot ? a.s2 : a.s1) + eo, base, lane, n, r.code[k]);
+            const uint8_t* cp = reinterpret_cast<const uint8_t*>(slot ? a.s2 : a.s1) + eo;
+#pragma unroll
+            for (int q = 0; q < R::NQ; ++q)
+                r.code[k][q] = ld_stream(reinterpret_cast<const uint32_t*>(cp + L::elem(base, lane, q)));
             const float* am = (slot ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
 #pragma unroll
-            for (int b = 0; b < R::BPT; ++b) r.A[k][b] = (FULL || blk0 + b < a.nb) ? am[blk0 + b] : 0.0f;
+            for (int b = 0; b < R::BPT; ++b) r.A[k][b] = gbl(am)[blk0 + b];
         } else {
             const float* fp = reinterpret_cast<const float*>(slot ? a.s2 : a.s1) + eo;
 #pragma unroll
-            for (int q = 0; q < R::NQ; ++q) {
-                const int64_t e = L::elem(base, lane, q);
-                if constexpr (FULL) {
-                    r.fst[k][q] = ld_stream(reinterpret_cast<const f32x4*>(fp + e));
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) r.fst[k][q][i] = e + i < n ? fp[e + i] : 0.0f;
-                }
-            }
+            for (int q = 0; q < R::NQ; ++q)
+                r.fst[k][q] = ld_stream(reinterpret_cast<const f32x4*>(fp + L::elem(base, lane, q)));
 #pragma unroll
             for (int b = 0; b < R::BPT; ++b) r.A[k][b] = 0.0f;
         }
     }
 }
 
-// Compute and store one tile from its raw inputs.
-template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool FAST, bool FULL>
+// Compute and store one full tile from its raw inputs.
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool FAST>
 __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1, const MapLDS& M2,
                                              int64_t base, int lane, const TileRaw<DT, OPT, BS, QUANT>& r) {
     using L = Layout<BS>;
@@ -588,18 +607,15 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
             const float* Q = slot ? M2.Q : M1.Q;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float v;
-                if constexpr (QUANT) v = Q[(r.code[k][q] >> (8 * i)) & 0xffu] * r.A[k][q / QPB];
-                else v = r.fst[k][q][i];
-                st[k][q][i] = (FULL || e + i < n) ? v : 0.0f;
+                if constexpr (QUANT) st[k][q][i] = Q[(r.code[k][q] >> (8 * i)) & 0xffu] * r.A[k][q / QPB];
+                else st[k][q][i] = r.fst[k][q][i];
             }
         }
         // element updates
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool valid = FULL || (e + i < n);
             const bool skip = SKIP && (gq[i] == 0.0f);   // raw gradient; -0 counts as zero
-            live[q][i] = valid && !skip;
+            live[q][i] = !skip;
             any_live[q / QPB] = any_live[q / QPB] || live[q][i];
             float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
                            NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
@@ -612,14 +628,8 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
         if constexpr (!SKIP && !UNORM) {
             // nothing waits on the block: write this quad's parameters now
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pf[q][i] = live[q][i] ? apply_step<OPT>(a.s, pf[q][i], dl[q][i]) : pf[q][i];
-            if constexpr (FULL) {
-                store4<DT>(a.p, e, pf[q]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (e + i < n) store1<DT>(a.p, e + i, pf[q][i]);
-            }
+            for (int i = 0; i < 4; ++i) pf[q][i] = apply_step<OPT>(a.s, pf[q][i], dl[q][i]);
+            store4<DT>(a.p, e, pf[q]);
         }
     }
 
@@ -627,7 +637,7 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
     bool write[BPT];
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-        write[b] = (FULL || blk0 + b < a.nb) && (!SKIP || wave_any(any_live[b]));
+        write[b] = !SKIP || wave_any(any_live[b]);
         if constexpr (UNORM) {
             double su = 0.0, sp = 0.0;
 #pragma unroll
@@ -658,16 +668,9 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             if (!write[q / QPB]) continue;                 // wave-uniform
-            const int64_t e = L::elem(base, lane, q);
 #pragma unroll
             for (int i = 0; i < 4; ++i) pf[q][i] = live[q][i] ? apply_step<OPT>(a.s, pf[q][i], dl[q][i]) : pf[q][i];
-            if constexpr (FULL) {
-                store4<DT>(a.p, e, pf[q]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (e + i < n) store1<DT>(a.p, e + i, pf[q][i]);
-            }
+            store4<DT>(a.p, L::elem(base, lane, q), pf[q]);
         }
     }
 
@@ -684,93 +687,327 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
             uint8_t* cp = reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + eo;
 #pragma unroll
             for (int b = 0; b < BPT; ++b)
-                if (write[b] && lane == 0) am[blk0 + b] = A[b];
+                if (write[b] && lane == 0) gbl(am)[blk0 + b] = A[b];
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                if (write[q / QPB]) store_code_word<FULL>(cp, L::elem(base, lane, q), n, w[q]);
+                if (write[q / QPB]) store_code_word<true>(cp, L::elem(base, lane, q), n, w[q]);
         } else {
             float* fp = reinterpret_cast<float*>(slot ? a.s2 : a.s1) + eo;
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 if (!write[q / QPB]) continue;
-                const int64_t e = L::elem(base, lane, q);
-                if constexpr (FULL) {
-                    const f32x4 v = {st[k][q][0], st[k][q][1], st[k][q][2], st[k][q][3]};
-                    st_stream(v, reinterpret_cast<f32x4*>(fp + e));
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (e + i < n) fp[e + i] = st[k][q][i];
-                }
+                const f32x4 v = {st[k][q][0], st[k][q][1], st[k][q][2], st[k][q][3]};
+                st_stream(v, reinterpret_cast<f32x4*>(fp + L::elem(base, lane, q)));
             }
         }
     }
 }
+
+// ---------------------------------------------------------------- guarded tiles
+
+// Lane j's value of v (wave-uniform).
+__device__ __forceinline__ float lane_value(float v, int j) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
+// One quad of a quad-at-a-time tile: the loads (VEC: one vector access per array;
+// otherwise element-wise, values past n read as zero), the decoded states and the
+// element updates, exactly as a full tile computes them.  Returns the live
+// elements as bits 0-3.  Both passes of guarded_tile call it, so the second pass
+// recomputes what the first one saw.
+template <int DT, int OPT, bool QUANT, bool SKIP, bool VEC>
+__device__ __forceinline__ uint32_t guarded_quad(const StepArgs& a, const MapLDS& M1, const MapLDS& M2, int64_t e,
+                                                 const float (&A)[NumStates<OPT>::v], float (&pv)[4],
+                                                 float (&st)[NumStates<OPT>::v][4], float (&dl)[4]) {
+    constexpr int NS = NumStates<OPT>::v;
+    const int64_t n = a.n;
+    float gv[4];
+    if constexpr (VEC) {
+        load4<DT>(a.p, e, pv);
+        load4<DT>(a.g, e, gv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool valid = e + i < n;
+            pv[i] = valid ? load1<DT>(a.p, e + i) : 0.0f;
+            gv[i] = valid ? load1<DT>(a.g, e + i) : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int slot = Slot<OPT>::which(k);
+        const int64_t eo = Slot<OPT>::elem_off(k, n);
+        if constexpr (QUANT) {
+            const uint8_t* cp = reinterpret_cast<const uint8_t*>(slot ? a.s2 : a.s1) + eo;
+            const float* Q = slot ? M2.Q : M1.Q;
+            if constexpr (VEC) {
+                const uint32_t w = ld_stream(reinterpret_cast<const uint32_t*>(cp + e));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[k][i] = Q[(w >> (8 * i)) & 0xffu] * A[k];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[k][i] = e + i < n ? Q[gbl(cp)[e + i]] * A[k] : 0.0f;
+            }
+        } else {
+            const float* fp = reinterpret_cast<const float*>(slot ? a.s2 : a.s1) + eo;
+            if constexpr (VEC) {
+                const f32x4 v = ld_stream(reinterpret_cast<const f32x4*>(fp + e));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[k][i] = v[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[k][i] = e + i < n ? gbl(fp)[e + i] : 0.0f;
+            }
+        }
+    }
+    uint32_t livem = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool valid = VEC || e + i < n;
+        const bool skip = SKIP && (gv[i] == 0.0f);
+        const bool live = valid && !skip;
+        livem |= live ? 1u << i : 0u;
+        float s3[3] = {st[0][i], NS > 1 ? st[NS > 1 ? 1 : 0][i] : 0.0f, NS > 2 ? st[NS > 2 ? 2 : 0][i] : 0.0f};
+        float d;
+        update_elem<OPT>(a.s, pv[i], gv[i], s3, d);
+        dl[i] = live ? d : 0.0f;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) st[k][i] = live ? s3[k] : st[k][i];
+    }
+    return livem;
+}
+
+// A tile one quad at a time: ragged or misaligned tiles (VEC false: element-wise
+// accesses), and every full tile when the maps need the binary-search encoder (VEC
+// true), whose register footprint would otherwise set the whole kernel's.  Pass 1
+// reads the inputs and forms what each block needs (new absmax, whether anything
+// is written, update norms) as its last quad goes by; pass 2 reads them again,
+// recomputes, encodes and stores.  The results are those of a full tile holding
+// the same values (elements past n count as zeros and are never written).  The
+// loops stay rolled and per-block values live in lane b of a register, so the
+// path adds little to the kernel's register footprint.
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool FAST, bool VEC>
+__device__ __forceinline__ void guarded_tile(const StepArgs& a, const MapLDS& M1, const MapLDS& M2,
+                                             int64_t base, int lane) {
+    using L = Layout<BS>;
+    constexpr int NQ = L::NQ, BPT = L::BPT, QPB = L::QPB;
+    constexpr int NS = NumStates<OPT>::v;
+    const int64_t n = a.n;
+    const int64_t blk0 = base / BS;
+    // An opaque copy of the lane index: without it the compiler hoists this path's
+    // lane-derived addresses out of the tile loop, and they then occupy registers
+    // through the full-tile path as well.
+    asm volatile("" : "+v"(lane));
+
+    // lane b: block b's old absmax, new absmax and its reciprocal, clip factor
+    float A0v[NS], Av[NS], rv[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const float* am = (Slot<OPT>::which(k) ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
+        A0v[k] = (QUANT && lane < BPT && blk0 + lane < a.nb) ? gbl(am)[blk0 + lane] : 0.0f;
+        Av[k] = 0.0f;
+        rv[k] = 0.0f;
+    }
+    float clipv = 1.0f;
+    uint32_t wmask = 0, cmask = 0;     // blocks written / clipped (uniform)
+
+    if constexpr (QUANT || SKIP || UNORM) {
+        float mcur[NS];
+        uint32_t anycur = 0;
+        double su = 0.0, sp = 0.0;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) mcur[k] = 0.0f;
+#pragma unroll 1
+        for (int q = 0; q < NQ; ++q) {
+            const int qb = q / QPB;
+            float Ab[NS], pv[4], st[NS][4], dl[4];
+#pragma unroll
+            for (int k = 0; k < NS; ++k) Ab[k] = lane_value(A0v[k], qb);
+            anycur |= guarded_quad<DT, OPT, QUANT, SKIP, VEC>(a, M1, M2, L::elem(base, lane, q), Ab, pv, st, dl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int k = 0; k < NS; ++k) mcur[k] = fmaxf(mcur[k], fabsf(st[k][i]));
+                if constexpr (UNORM) {
+                    const float d2 = dl[i] * dl[i];
+                    const float p2 = pv[i] * pv[i];
+                    su += (double)d2;
+                    sp += (double)p2;
+                }
+            }
+            if (q % QPB != QPB - 1) continue;               // block qb not complete yet
+            if (blk0 + qb < a.nb && (!SKIP || wave_any(anycur != 0u))) wmask |= 1u << qb;
+            if constexpr (UNORM) {
+                const double U = sqrt(wave_sum_f64(su)), P = sqrt(wave_sum_f64(sp));
+                const double lim = (double)a.s.max_unorm * P;
+                if (U > lim) {
+                    cmask |= 1u << qb;
+                    clipv = lane == qb ? (float)(lim / U) : clipv;
+                }
+            }
+            if constexpr (QUANT) {
+#pragma unroll
+                for (int k = 0; k < NS; ++k) {
+                    const float u = wave_max_nonneg(mcur[k]);
+                    Av[k] = lane == qb ? u : Av[k];
+                    rv[k] = lane == qb ? ((u == 0.0f) ? 0.0f : 1.0f / u) : rv[k];
+                    mcur[k] = 0.0f;
+                }
+            }
+            anycur = 0;
+            su = 0.0;
+            sp = 0.0;
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < BPT; ++b)
+            if (blk0 + b < a.nb) wmask |= 1u << b;
+    }
+
+#pragma unroll 1
+    for (int q = 0; q < NQ; ++q) {
+        const int qb = q / QPB;
+        if (!((wmask >> qb) & 1u)) continue;                 // wave-uniform
+        const int64_t e = L::elem(base, lane, q);
+        float Ab[NS], pv[4], st[NS][4], dl[4];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) Ab[k] = lane_value(A0v[k], qb);
+        const uint32_t livem = guarded_quad<DT, OPT, QUANT, SKIP, VEC>(a, M1, M2, e, Ab, pv, st, dl);
+        if constexpr (UNORM) {
+            if ((cmask >> qb) & 1u) {
+                const float c = lane_value(clipv, qb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dl[i] = dl[i] * c;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = ((livem >> i) & 1u) ? apply_step<OPT>(a.s, pv[i], dl[i]) : pv[i];
+        if constexpr (VEC) {
+            store4<DT>(a.p, e, pv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (e + i < n) store1<DT>(a.p, e + i, pv[i]);
+        }
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const int slot = Slot<OPT>::which(k);
+            const int64_t eo = Slot<OPT>::elem_off(k, n);
+            if constexpr (QUANT) {
+                const float rb = lane_value(rv[k], qb);
+                uint32_t w = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w |= encode<FAST>(slot ? M2 : M1, st[k][i] * rb) << (8 * i);
+                store_code_word<VEC>(reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + eo, e, n, w);
+            } else {
+                float* fp = reinterpret_cast<float*>(slot ? a.s2 : a.s1) + eo;
+                if constexpr (VEC) {
+                    const f32x4 v = {st[k][0], st[k][1], st[k][2], st[k][3]};
+                    st_stream(v, reinterpret_cast<f32x4*>(fp + e));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (e + i < n) gbl(fp)[e + i] = st[k][i];
+                }
+            }
+        }
+    }
+    if constexpr (QUANT) {
+        if (lane < BPT && ((wmask >> lane) & 1u)) {
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                float* am = (Slot<OPT>::which(k) ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
+                gbl(am)[blk0 + lane] = Av[k];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- tile loop and kernel
 
 // Index of this wave in the grid, as a scalar (wave-uniform) value.
 __device__ __forceinline__ int64_t wave_id() {
     return (int64_t)blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-// The tiles of one wave: t = first, first + stride, ...  Each tile issues all of
-// its loads before any use; latency is hidden by the other waves of the CU (the
-// tile code needs few enough registers for five waves per SIMD, which streams
-// better here than a two-deep software pipeline at two waves per SIMD).  Tiles in
-// range on aligned buffers take the vector path, the ragged last tile (or every
-// tile of an unaligned call) the guarded path.
-template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool FAST>
+// Multi-tensor launches: the tensor holding global tile gt and the tile's index in
+// it -- the last table entry whose first tile is <= gt, by binary search over the
+// first-tile indices staged in LDS.  The table is constant while the kernel runs,
+// so its entries are read through the constant address space (scalar loads).
+#define BITOPT_CONSTANT __attribute__((address_space(4)))
+__device__ __forceinline__ int64_t resolve_tile(const StepArgs& a0, const int64_t* T0, int64_t gt, StepArgs& a) {
+    int lo = 0, hi = a0.ntab - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (T0[mid] <= gt) lo = mid; else hi = mid - 1;
+    }
+    const BITOPT_CONSTANT TensorDesc* tab = (const BITOPT_CONSTANT TensorDesc*)a0.table;
+    const BITOPT_CONSTANT TensorDesc& d = tab[__builtin_amdgcn_readfirstlane(lo)];
+    a = a0;
+    a.p = d.p; a.g = d.g; a.s1 = d.s1; a.s2 = d.s2; a.a1 = d.a1; a.a2 = d.a2;
+    a.n = d.n; a.nb = d.nb; a.vec = d.vec;
+    return gt - d.tile0;
+}
+
+template <int BS, bool MULTI>
+__device__ __forceinline__ int64_t total_tiles(const StepArgs& a) {
+    if constexpr (MULTI) return a.total_tiles;
+    else return (a.n + Layout<BS>::TE - 1) / Layout<BS>::TE;
+}
+
+// The tiles of one wave: gt = first, first + stride, ...  A full tile issues all of
+// its loads before any use; latency is hidden by the other waves of the CU.
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool MULTI, bool FAST>
 __device__ __forceinline__ void step_tiles(const StepArgs& a0, const MapLDS& M1, const MapLDS& M2,
                                            const int64_t* T0) {
-    using R = TileRaw<DT, OPT, BS, QUANT>;
     constexpr int64_t TE = Layout<BS>::TE;
+    // the binary-search encoder runs on the quad-at-a-time path (see guarded_tile)
+    constexpr bool WHOLE = !QUANT || FAST;
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerGroup;
-    const int64_t ntiles = a0.table ? a0.total_tiles : (a0.n + TE - 1) / TE;
+    const int64_t ntiles = total_tiles<BS, MULTI>(a0);
     for (int64_t gt = wave_id(); gt < ntiles; gt += stride) {
-        StepArgs a = a0;
+        StepArgs am;
         int64_t t = gt;
-        if (a0.table) {
-            // the tensor holding global tile gt: the last one whose first tile is <= gt
-            int lo = 0, hi = a0.ntab - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (T0[mid] <= gt) lo = mid; else hi = mid - 1;
+        if constexpr (MULTI) t = resolve_tile(a0, T0, gt, am);
+        const StepArgs& a = MULTI ? am : a0;
+        if (tile_full<BS>(a, t)) {
+            if constexpr (WHOLE) {
+                TileRaw<DT, OPT, BS, QUANT> x;
+                load_tile<DT, OPT, BS, QUANT>(a, t * TE, lane, x);
+                process_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST>(a, M1, M2, t * TE, lane, x);
+            } else {
+                guarded_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST, true>(a, M1, M2, t * TE, lane);
             }
-            const TensorDesc& d = a0.table[__builtin_amdgcn_readfirstlane(lo)];
-            a.p = d.p; a.g = d.g; a.s1 = d.s1; a.s2 = d.s2; a.a1 = d.a1; a.a2 = d.a2;
-            a.n = d.n; a.nb = d.nb; a.vec = d.vec;
-            t = gt - d.tile0;
-        }
-        R x;
-        if (a.vec && (t + 1) * TE <= a.n) {
-            load_tile<DT, OPT, BS, QUANT, true>(a, t * TE, lane, x);
-            process_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST, true>(a, M1, M2, t * TE, lane, x);
         } else {
-            load_tile<DT, OPT, BS, QUANT, false>(a, t * TE, lane, x);
-            process_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST, false>(a, M1, M2, t * TE, lane, x);
+            guarded_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST, false>(a, M1, M2, t * TE, lane);
         }
     }
 }
 
-template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM>
+// One launch of the fused step: a single tensor (MULTI false: the launch arguments)
+// or every tensor of a descriptor table (MULTI true).
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
     constexpr int NMAPS = (OPT == kAdam || OPT == kAdemamix) ? 2 : 1;
     __shared__ float Q1[256], Q2[256], T1[256], T2[256];
     __shared__ __attribute__((aligned(16))) uint8_t B1[search::kNB];
     __shared__ __attribute__((aligned(16))) uint8_t B2[search::kNB];
-    __shared__ int64_t T0[kMaxTableTensors];
+    __shared__ uint32_t vote[kWavesPerGroup];
+    __shared__ int64_t T0[MULTI ? kMaxTableTensors : 1];
     const MapLDS M1{Q1, T1, B1}, M2{Q2, T2, B2};
-    if (a.table) {
-        for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = a.table[i].tile0;
+    if constexpr (MULTI) {
+        const BITOPT_CONSTANT TensorDesc* tab = (const BITOPT_CONSTANT TensorDesc*)a.table;
+        for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = tab[i].tile0;
         __syncthreads();
     }
     if constexpr (QUANT) {
-        if (stage_maps<NMAPS>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2))
-            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, true>(a, M1, M2, T0);
+        if (stage_maps<NMAPS>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote))
+            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, MULTI, true>(a, M1, M2, T0);
         else
-            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, false>(a, M1, M2, T0);
+            step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, MULTI, false>(a, M1, M2, T0);
     } else {
-        step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, false>(a, M1, M2, T0);
+        step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, MULTI, false>(a, M1, M2, T0);
     }
 }
 
@@ -808,7 +1045,7 @@ __device__ __forceinline__ void quant_tile(const CodecArgs& a, const MapLDS& M, 
     encode_tile<BS, FAST>(M, v, w, A);
 #pragma unroll
     for (int b = 0; b < L::BPT; ++b)
-        if ((FULL || blk0 + b < a.nb) && lane == 0) a.absmax[blk0 + b] = A[b];
+        if ((FULL || blk0 + b < a.nb) && lane == 0) gbl(a.absmax)[blk0 + b] = A[b];
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
         if (FULL || blk0 + q / L::QPB < a.nb) store_code_word<FULL>(a.codes, L::elem(base, lane, q), n, w[q]);
@@ -831,8 +1068,9 @@ template <int DT, int BS>
 __global__ __launch_bounds__(kThreads) void k_quantize(CodecArgs a) {
     __shared__ float Q[256], T[256];
     __shared__ __attribute__((aligned(16))) uint8_t B[search::kNB];
+    __shared__ uint32_t vote[kWavesPerGroup];
     const MapLDS M{Q, T, B};
-    if (stage_maps<1>(a.qmap, nullptr, Q, nullptr, T, nullptr, B, nullptr)) quant_tiles<DT, BS, true>(a, M);
+    if (stage_maps<1>(a.qmap, nullptr, Q, nullptr, T, nullptr, B, nullptr, vote)) quant_tiles<DT, BS, true>(a, M);
     else quant_tiles<DT, BS, false>(a, M);
 }
 
@@ -840,13 +1078,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize(CodecArgs a) {
 template <int DT, int BS>
 __global__ __launch_bounds__(kThreads) void k_dequantize(CodecArgs a) {
     __shared__ float Q[256];
-    Q[threadIdx.x] = a.qmap[threadIdx.x];
+    Q[threadIdx.x] = gbl(a.qmap)[threadIdx.x];
     __syncthreads();
     const int64_t nquads = (a.n + 3) / 4;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t qd = (int64_t)blockIdx.x * kThreads + threadIdx.x; qd < nquads; qd += stride) {
         const int64_t e = qd * 4;
-        const float A = a.absmax[e / BS];             // 4 | BS: one block per quad
+        const float A = gbl(a.absmax)[e / BS];        // 4 | BS: one block per quad
         float v[4];
         if (a.vec && e + 4 <= a.n) {
             const uint32_t w = ld_stream(reinterpret_cast<const uint32_t*>(a.codes + e));
@@ -856,7 +1094,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(CodecArgs a) {
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (e + i < a.n) store1<DT>(a.out, e + i, Q[a.codes[e + i]] * A);
+                if (e + i < a.n) store1<DT>(a.out, e + i, Q[gbl(a.codes)[e + i]] * A);
         }
     }
 }

@@ -10,8 +10,11 @@ namespace bitopt {
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM>
 hipError_t launch_one(const StepArgs& a, hipStream_t s) {
     constexpr int64_t tile = Layout<BS>::TE;
-    const int64_t work = a.table ? a.total_tiles * tile : a.n;
-    hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM>), tile_grid(work, tile), dim3(kThreads), 0, s, a);
+    if (a.table)
+        hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM, true>), tile_grid(a.total_tiles * tile, tile),
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM, false>), tile_grid(a.n, tile), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

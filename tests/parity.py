@@ -94,7 +94,9 @@ class Compare:
 class Quant8:
     """One tensor's 8-bit optimizer state on the device and in the oracle."""
 
-    def __init__(self, hp: dict, p0: np.ndarray, dtype: str):
+    def __init__(self, hp: dict, p0: np.ndarray, dtype: str, maps=None):
+        """maps: optional (qmap1, qmap2) float32 arrays used on both sides in place of
+        the standard signed/unsigned maps."""
         self.hp = dict(hp)
         self.dtype = dtype
         self.n = n = p0.size
@@ -104,6 +106,9 @@ class Quant8:
         self.k1 = 2 if opt == "ademamix" else 1
         self.two = n_states(opt) >= 2
         q1, q2 = oracle.dynamic_map(True), oracle.dynamic_map(False)
+        if maps is not None:
+            q1 = maps[0] if maps[0] is not None else q1
+            q2 = maps[1] if maps[1] is not None else q2
         # oracle side
         self.o = dict(p=p0.copy(), s1=np.zeros(self.k1 * n, np.uint8), a1=np.zeros(self.k1 * nb, np.float32),
                       s2=np.zeros(n, np.uint8) if self.two else None,
@@ -112,6 +117,9 @@ class Quant8:
         self.d = dict(p=to_dev(p0, dtype), s1=torch.zeros(self.k1 * n, dtype=torch.uint8, device="cuda"),
                       a1=torch.zeros(self.k1 * nb, dtype=torch.float32, device="cuda"),
                       q1=bitopt.create_dynamic_map(True).cuda(), q2=bitopt.create_dynamic_map(False).cuda())
+        if maps is not None:
+            self.d["q1"] = torch.from_numpy(np.ascontiguousarray(q1, np.float32)).cuda()
+            self.d["q2"] = torch.from_numpy(np.ascontiguousarray(q2, np.float32)).cuda()
         if self.two:
             self.d["s2"] = torch.zeros(n, dtype=torch.uint8, device="cuda")
             self.d["a2"] = torch.zeros(nb, dtype=torch.float32, device="cuda")

@@ -45,11 +45,12 @@ def _grad(seed, t, n, dtype, zero_frac=0.0, B=256):
     return W.to_dtype(g, dtype)
 
 
-def _run(hp, n, dtype, steps, seed, zero_frac=0.0):
+def _run(hp, n, dtype, steps, seed, zero_frac=0.0, maps=None):
     print(f"\n[case] {hp['optimizer']} {dtype} B={hp['blocksize']} n={n} steps={steps} "
-          f"skip={hp.get('skip_zeros', False)} max_unorm={hp.get('max_unorm', 0.0)}", flush=True)
+          f"skip={hp.get('skip_zeros', False)} max_unorm={hp.get('max_unorm', 0.0)} "
+          f"maps={'custom' if maps is not None else 'standard'}", flush=True)
     p0 = W.to_dtype(W.normal_f32([seed, 1], n, 0.02), dtype)
-    q = Quant8(hp, p0, dtype)
+    q = Quant8(hp, p0, dtype, maps)
     cmp = Compare()
     for t in range(1, steps + 1):
         g = _grad(seed, t, n, dtype, zero_frac, hp["blocksize"])
@@ -80,6 +81,42 @@ def test_step_8bit_skip_zeros(name, dtype, bs):
 @pytest.mark.parametrize("name", list(OPTS))
 def test_step_8bit_max_unorm(name):
     _run(dict(OPTS[name], blocksize=256, max_unorm=0.002), RAGGED[256], "f32", 3, 300)
+
+
+def _jittered_map(signed, seed):
+    """A sorted 256-entry map close to a standard one but equal to neither standard
+    map, so the kernels take the binary-search encoder."""
+    q = oracle.dynamic_map(signed).astype(np.float64)
+    rng = np.random.default_rng(seed)
+    inner = (q != 0) & (np.abs(q) != 1)
+    q[inner] *= 1 + 2e-3 * rng.uniform(-1, 1, int(inner.sum()))
+    q = np.sort(q).astype(np.float32)
+    assert np.all(np.diff(q) > 0)
+    return q
+
+
+@pytest.mark.parametrize("bs", [256, 2048])
+@pytest.mark.parametrize("name", list(OPTS))
+def test_step_8bit_custom_maps(name, bs):
+    """Maps that are not the standard ones: binary-search encoder, full and ragged tiles."""
+    dtype = "bf16" if name == "ademamix" else "f32"
+    maps = (_jittered_map(True, 11), _jittered_map(False, 12))
+    _run(dict(OPTS[name], blocksize=bs), RAGGED[bs], dtype, 3, 900 + bs, maps=maps)
+
+
+def test_step_8bit_custom_maps_skip_unorm():
+    maps = (_jittered_map(True, 13), _jittered_map(False, 14))
+    _run(dict(OPTS["adam"], blocksize=256, skip_zeros=True, max_unorm=0.002), RAGGED[256], "f16", 3, 960,
+         zero_frac=0.3, maps=maps)
+
+
+def test_step_8bit_standard_maps_other_assignment():
+    """Standard maps passed in other slots than (signed, unsigned): the kernels stage
+    the matching search tables again and keep the table encoder."""
+    s, u = oracle.dynamic_map(True), oracle.dynamic_map(False)
+    _run(dict(OPTS["adam"], blocksize=256), RAGGED[256], "f32", 3, 950, maps=(s, s))
+    _run(dict(OPTS["adam"], blocksize=2048), RAGGED[2048], "f32", 3, 951, maps=(u, s))
+    _run(dict(OPTS["momentum"], blocksize=256), RAGGED[256], "f16", 3, 952, maps=(u, None))
 
 
 @pytest.mark.parametrize("n", [1, 3, 255, 256, 257, 1023, 1025, 2047, 2049])
