@@ -104,16 +104,19 @@ bitopt::StepScalars make_scalars(const bitopt_hparams& h, int32_t t) {
 
 namespace bitopt {
 
-// Compute units of each device, queried on first use.  Groups per CU: enough
-// 4-wave groups to fill the CU at the step kernels' occupancy with a few tiles per
-// wave, so the LDS codebook staging is paid a few times per CU, not per tile.
+// Compute units of each device, queried on first use.  Groups per CU: 64 4-wave
+// groups, i.e. one tile per wave up to 16 M elements (B = 256) on 256 CUs, and a
+// grid stride beyond that, so very large launches stage the LDS codebooks once per
+// group for many tiles rather than once per tile.  Measured on MI355X: one tile per
+// wave streams best (the hardware refills CUs as groups retire); the cap matters
+// only for launches of hundreds of millions of elements.
 int64_t group_cap() {
     constexpr int kMaxDev = 64;
     static std::atomic<int> cus[kMaxDev];
     static const int per_cu = [] {
         const char* e = std::getenv("BITOPT_GROUPS_PER_CU");
         const int v = e ? std::atoi(e) : 0;
-        return v > 0 ? v : 4;
+        return v > 0 ? v : 64;
     }();
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 2048;

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "bitopt_tables.h"   // generated: constant search tables of the standard maps
 #include "search_layout.h"
 
@@ -183,24 +185,29 @@ template <int DT> __device__ __forceinline__ void store1(void* base, int64_t e, 
 
 // ---------------------------------------------------------------- wave reductions
 
+// Maxima of non-negative floats are taken on their bit patterns as integers (the
+// same order), which avoids the NaN-quieting moves a float max needs on values that
+// arrive through lane exchanges.
+
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_or_zero(float v) {
+__device__ __forceinline__ int dpp_or_zero(int v) {
     // Lanes whose source lane is outside the pattern, or whose row is masked off,
     // read 0 (the identity of a max over non-negative values).
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
 }
 
 // Max over the 64 lanes of non-negative values; the result is wave-uniform.
 // row_shr 1,2,4,8 leave each row's max in its lane 15; row_bcast15 and row_bcast31
 // carry it across rows into lane 63, which is then read as a scalar.
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-    v = fmaxf(v, dpp_or_zero<0x111, 0xF>(v));
-    v = fmaxf(v, dpp_or_zero<0x112, 0xF>(v));
-    v = fmaxf(v, dpp_or_zero<0x114, 0xF>(v));
-    v = fmaxf(v, dpp_or_zero<0x118, 0xF>(v));
-    v = fmaxf(v, dpp_or_zero<0x142, 0xA>(v));
-    v = fmaxf(v, dpp_or_zero<0x143, 0xC>(v));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+__device__ __forceinline__ float wave_max_nonneg(float f) {
+    int v = __float_as_int(f);
+    v = max(v, dpp_or_zero<0x111, 0xF>(v));
+    v = max(v, dpp_or_zero<0x112, 0xF>(v));
+    v = max(v, dpp_or_zero<0x114, 0xF>(v));
+    v = max(v, dpp_or_zero<0x118, 0xF>(v));
+    v = max(v, dpp_or_zero<0x142, 0xA>(v));
+    v = max(v, dpp_or_zero<0x143, 0xC>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 
 __device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
@@ -215,15 +222,15 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 // Max over the 16 lanes of each DPP row (every lane ends with its row's max).
 template <int CTRL>
-__device__ __forceinline__ float dpp_rot(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+__device__ __forceinline__ int dpp_rot(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
-__device__ __forceinline__ float row_max_nonneg(float v) {
-    v = fmaxf(v, dpp_rot<0x128>(v));    // row_ror 8, 4, 2, 1
-    v = fmaxf(v, dpp_rot<0x124>(v));
-    v = fmaxf(v, dpp_rot<0x122>(v));
-    v = fmaxf(v, dpp_rot<0x121>(v));
+__device__ __forceinline__ int row_max_nonneg(int v) {
+    v = max(v, dpp_rot<0x128>(v));    // row_ror 8, 4, 2, 1
+    v = max(v, dpp_rot<0x124>(v));
+    v = max(v, dpp_rot<0x122>(v));
+    v = max(v, dpp_rot<0x121>(v));
     return v;
 }
 
@@ -342,36 +349,75 @@ __device__ __forceinline__ bool stage_maps(const float* q1, const float* q2, flo
 
 // ---------------------------------------------------------------- optimizer updates
 
+// Correctly rounded square root for v == 0 and v >= 2^-96 (and +inf, NaN): the hardware
+// estimate, within one ulp, is moved to a neighbour when the fused residual
+// v - neighbour * estimate shows that neighbour is the rounded root.  This is the
+// general correctly rounded expansion without its input scaling and its final
+// zero/infinity select, and gives the same bits wherever that scaling is not
+// applied; positive v below 2^-96 need the scaling (see sqrt_needs_scaling).
+__device__ __forceinline__ float sqrt_rn_unscaled(float v) {
+    const float s = __builtin_amdgcn_sqrtf(v);
+    const float dn = __uint_as_float(__float_as_uint(s) - 1u);
+    const float up = __uint_as_float(__float_as_uint(s) + 1u);
+    const float rdn = __builtin_fmaf(-dn, s, v);
+    const float rup = __builtin_fmaf(-up, s, v);
+    const float r = rdn <= 0.0f ? dn : s;
+    return rup > 0.0f ? up : r;
+}
+// v in (0, 2^-96) (as bits of a non-negative float: 1 .. 0x0F7FFFFF)
+__device__ __forceinline__ bool sqrt_needs_scaling(float v) {
+    return __float_as_uint(v) - 1u < 0x0F7FFFFFu;
+}
+
+// Optimizers whose step divides by a root of the second moment.
+template <int OPT> struct HasRoot { static constexpr bool v = OPT == kAdam || OPT == kAdemamix; };
+// Index of the second moment (v, nu) in the state vector.
+template <int OPT> struct RootState { static constexpr int v = OPT == kAdemamix ? 2 : 1; };
+
+// Adam/AdEMAMix: the new states (Adam {m, v}; AdEMAMix {m1, m2, nu}).
+template <int OPT>
+__device__ __forceinline__ void moments(const StepScalars& s, float g, float st[3]) {
+    float t1, t2;
+    if constexpr (OPT == kAdam) {
+        t1 = s.b1 * st[0]; t2 = s.omb1 * g; st[0] = t1 + t2;
+        const float gg = g * g;
+        t1 = s.b2 * st[1]; t2 = s.omb2 * gg; st[1] = t1 + t2;
+    } else {
+        static_assert(OPT == kAdemamix, "moments of a root optimizer");
+        t1 = s.b1 * st[0]; t2 = s.omb1 * g; st[0] = t1 + t2;
+        t1 = s.b3t * st[1]; t2 = s.omb3 * g; st[1] = t1 + t2;
+        const float gg = g * g;
+        t1 = s.b2 * st[2]; t2 = s.omb2 * gg; st[2] = t1 + t2;
+    }
+}
+
+// Adam/AdEMAMix: the parameter step from the new states, d = lr * u with
+// u = (m * ic1 [+ alpha_t * m2]) / (sqrt(v) * rs2 + eps).  UNSCALED: the caller has
+// checked that no second moment needs the scaled square root.
+template <int OPT, bool UNSCALED>
+__device__ __forceinline__ float root_delta(const StepScalars& s, const float st[3]) {
+    const float v = st[RootState<OPT>::v];
+    const float r = UNSCALED ? sqrt_rn_unscaled(v) : sqrtf(v);
+    float den = r * s.rs2;
+    den = den + s.eps;
+    float num = st[0] * s.ic1;
+    if constexpr (OPT == kAdemamix) {
+        const float t2 = s.alpha_t * st[1];
+        num = num + t2;
+    }
+    const float u = num / den;
+    return s.lr * u;
+}
+
 // One element of one step.  st[] holds the decoded states on entry and the new
 // states on exit; the parameter step delta is returned through d.
-// Adam/AdamW: st = {m, v};  AdEMAMix: st = {m1, m2, nu};  Momentum: {buf};  Lion: {m}.
+// Adam/AdEMAMix: st = {m, v} / {m1, m2, nu};  Momentum: {buf};  Lion: {m}.
 template <int OPT>
 __device__ __forceinline__ void update_elem(const StepScalars& s, float p, float g, float st[3], float& d) {
     float t1, t2;
-    if constexpr (OPT == kAdam) {
-        float m = st[0], v = st[1];
-        t1 = s.b1 * m; t2 = s.omb1 * g; m = t1 + t2;
-        const float gg = g * g;
-        t1 = s.b2 * v; t2 = s.omb2 * gg; v = t1 + t2;
-        float den = sqrtf(v) * s.rs2;
-        den = den + s.eps;
-        const float mh = m * s.ic1;
-        const float u = mh / den;
-        d = s.lr * u;
-        st[0] = m; st[1] = v;
-    } else if constexpr (OPT == kAdemamix) {
-        float m1 = st[0], m2 = st[1], nu = st[2];
-        t1 = s.b1 * m1; t2 = s.omb1 * g; m1 = t1 + t2;
-        t1 = s.b3t * m2; t2 = s.omb3 * g; m2 = t1 + t2;
-        const float gg = g * g;
-        t1 = s.b2 * nu; t2 = s.omb2 * gg; nu = t1 + t2;
-        float den = sqrtf(nu) * s.rs2;
-        den = den + s.eps;
-        t1 = m1 * s.ic1; t2 = s.alpha_t * m2;
-        const float num = t1 + t2;
-        const float u = num / den;
-        d = s.lr * u;
-        st[0] = m1; st[1] = m2; st[2] = nu;
+    if constexpr (HasRoot<OPT>::v) {
+        moments<OPT>(s, g, st);
+        d = root_delta<OPT, false>(s, st);
     } else if constexpr (OPT == kMomentum) {
         float buf = st[0];
         t1 = s.wd * p;
@@ -424,8 +470,17 @@ template <int BS> struct Layout {
 // One block per tile: a wave max.  Four blocks per tile: a reduce-scatter -- two
 // exchanges between lane halves and row pairs leave row r with the partial max of
 // block r, a row reduction completes it, and one reciprocal serves all four blocks.
+// Normalization of a block with absmax u: values x map to (x * c) * r with one
+// correctly rounded reciprocal r = 1/(u * c) (r = 0 when u = 0).  c = 2^24 when u is
+// subnormal, whose plain reciprocal can exceed the fp32 range; otherwise c = 1,
+// i.e. the plain x * (1/u).  Both forms give the same bits wherever 1/u is finite.
+__device__ __forceinline__ void block_recip(float u, float& r, float& c) {
+    c = (u < 0x1p-126f) ? 0x1p24f : 1.0f;
+    r = (u == 0.0f) ? 0.0f : 1.0f / (u * c);
+}
+
 template <int BPT>
-__device__ __forceinline__ void block_absmax_lanes(const float (&m)[BPT], float& u, float& ru) {
+__device__ __forceinline__ void block_absmax_lanes(const float (&m)[BPT], float& u, float& ru, float& cu) {
     if constexpr (BPT == 1) {
         u = wave_max_nonneg(m[0]);
     } else {
@@ -433,16 +488,19 @@ __device__ __forceinline__ void block_absmax_lanes(const float (&m)[BPT], float&
         const int lane = threadIdx.x & 63;
         const bool hi = lane >= 32;
         const bool odd = (lane >> 4) & 1;
+        int mi[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) mi[b] = __float_as_int(m[b]);
         // lanes 0-31 keep blocks 0,1 and lanes 32-63 blocks 2,3
-        const float s0 = hi ? m[0] : m[2], s1 = hi ? m[1] : m[3];
-        const float k0 = hi ? m[2] : m[0], k1 = hi ? m[3] : m[1];
-        const float w0 = fmaxf(k0, __shfl_xor(s0, 32, 64));
-        const float w1 = fmaxf(k1, __shfl_xor(s1, 32, 64));
+        const int s0 = hi ? mi[0] : mi[2], s1 = hi ? mi[1] : mi[3];
+        const int k0 = hi ? mi[2] : mi[0], k1 = hi ? mi[3] : mi[1];
+        const int w0 = max(k0, __shfl_xor(s0, 32, 64));
+        const int w1 = max(k1, __shfl_xor(s1, 32, 64));
         // even rows keep the first of the pair, odd rows the second: row r -> block r
-        const float s = odd ? w0 : w1, k = odd ? w1 : w0;
-        u = row_max_nonneg(fmaxf(k, __shfl_xor(s, 16, 64)));
+        const int sx = odd ? w0 : w1, kx = odd ? w1 : w0;
+        u = __int_as_float(row_max_nonneg(max(kx, __shfl_xor(sx, 16, 64))));
     }
-    ru = (u == 0.0f) ? 0.0f : 1.0f / u;
+    block_recip(u, ru, cu);
 }
 
 // Block b's value of a pair left in lanes by block_absmax_lanes (wave-uniform).
@@ -454,13 +512,15 @@ __device__ __forceinline__ float block_value(float v, int b) {
 
 // The same as uniform per-block values.
 template <int BPT>
-__device__ __forceinline__ void block_absmax(const float (&m)[BPT], float (&A)[BPT], float (&r)[BPT]) {
-    float u, ru;
-    block_absmax_lanes<BPT>(m, u, ru);
+__device__ __forceinline__ void block_absmax(const float (&m)[BPT], float (&A)[BPT], float (&r)[BPT],
+                                             float (&c)[BPT]) {
+    float u, ru, cu;
+    block_absmax_lanes<BPT>(m, u, ru, cu);
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
         A[b] = block_value<BPT>(u, b);
         r[b] = block_value<BPT>(ru, b);
+        c[b] = block_value<BPT>(cu, b);
     }
 }
 
@@ -481,7 +541,7 @@ template <int BS, bool FAST, int NQ>
 __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ][4], uint32_t w[NQ],
                                             float (&A)[Layout<BS>::BPT]) {
     using L = Layout<BS>;
-    float m[L::BPT], r[L::BPT];
+    float m[L::BPT], r[L::BPT], c[L::BPT];
 #pragma unroll
     for (int b = 0; b < L::BPT; ++b) {
         float x = 0.0f;
@@ -491,18 +551,25 @@ __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ
             for (int i = 0; i < 4; ++i) x = fmaxf(x, fabsf(v[b * L::QPB + qq][i]));
         m[b] = x;
     }
-    block_absmax<L::BPT>(m, A, r);
+    block_absmax<L::BPT>(m, A, r, c);
+    bool scaled = false;                            // a subnormal block absmax (uniform)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const float rq = r[q / L::QPB];
-        uint32_t x = 0;
+    for (int b = 0; b < L::BPT; ++b) scaled = scaled || c[b] != 1.0f;
+    auto codes = [&](auto prescale) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float y = v[q][i] * rq;
-            x |= encode<FAST>(M, y) << (8 * i);
+        for (int q = 0; q < NQ; ++q) {
+            const float rq = r[q / L::QPB], cq = c[q / L::QPB];
+            uint32_t x = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float y = decltype(prescale)::value ? (v[q][i] * cq) * rq : v[q][i] * rq;
+                x |= encode<FAST>(M, y) << (8 * i);
+            }
+            w[q] = x;
         }
-        w[q] = x;
-    }
+    };
+    if (scaled) codes(std::true_type{});
+    else codes(std::false_type{});
 }
 
 // ---------------------------------------------------------------- fused step tile
@@ -593,10 +660,11 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
     bool any_live[BPT];
 #pragma unroll
     for (int b = 0; b < BPT; ++b) any_live[b] = false;
+    constexpr bool ROOT = HasRoot<OPT>::v;
+    constexpr bool EARLY = !SKIP && !UNORM;     // nothing waits on the block: store p per quad
 
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const int64_t e = L::elem(base, lane, q);
         float gq[4];
         widen_words<DT>(r.p[q], pf[q]);
         widen_words<DT>(r.g[q], gq);
@@ -611,7 +679,7 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
                 else st[k][q][i] = r.fst[k][q][i];
             }
         }
-        // element updates
+        // element updates (root optimizers: the new states first, then the step)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool skip = SKIP && (gq[i] == 0.0f);   // raw gradient; -0 counts as zero
@@ -619,17 +687,38 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
             any_live[q / QPB] = any_live[q / QPB] || live[q][i];
             float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
                            NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
-            float d;
-            update_elem<OPT>(a.s, pf[q][i], gq[i], s3, d);
-            dl[q][i] = live[q][i] ? d : 0.0f;
+            if constexpr (ROOT) {
+                moments<OPT>(a.s, gq[i], s3);
+            } else {
+                float d;
+                update_elem<OPT>(a.s, pf[q][i], gq[i], s3, d);
+                dl[q][i] = live[q][i] ? d : 0.0f;
+            }
 #pragma unroll
             for (int k = 0; k < NS; ++k) st[k][q][i] = live[q][i] ? s3[k] : st[k][q][i];
         }
-        if constexpr (!SKIP && !UNORM) {
-            // nothing waits on the block: write this quad's parameters now
+        if constexpr (ROOT) {
+            // The unscaled square root is exact unless a second moment of the quad lies
+            // in (0, 2^-96); then the quad takes the general one (same bits either way).
+            bool tiny = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tiny = tiny || sqrt_needs_scaling(st[RootState<OPT>::v][q][i]);
+            auto deltas = [&](auto unscaled) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
+                                         NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
+                    const float d = root_delta<OPT, decltype(unscaled)::value>(a.s, s3);
+                    dl[q][i] = live[q][i] ? d : 0.0f;
+                }
+            };
+            if (wave_any(tiny)) deltas(std::false_type{});
+            else deltas(std::true_type{});
+        }
+        if constexpr (EARLY) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pf[q][i] = apply_step<OPT>(a.s, pf[q][i], dl[q][i]);
-            store4<DT>(a.p, e, pf[q]);
+            store4<DT>(a.p, L::elem(base, lane, q), pf[q]);
         }
     }
 
@@ -799,14 +888,15 @@ __device__ __forceinline__ void guarded_tile(const StepArgs& a, const MapLDS& M1
     // through the full-tile path as well.
     asm volatile("" : "+v"(lane));
 
-    // lane b: block b's old absmax, new absmax and its reciprocal, clip factor
-    float A0v[NS], Av[NS], rv[NS];
+    // lane b: block b's old absmax, new absmax with its reciprocal and prescale, clip factor
+    float A0v[NS], Av[NS], rv[NS], cv[NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
         const float* am = (Slot<OPT>::which(k) ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
         A0v[k] = (QUANT && lane < BPT && blk0 + lane < a.nb) ? gbl(am)[blk0 + lane] : 0.0f;
         Av[k] = 0.0f;
         rv[k] = 0.0f;
+        cv[k] = 1.0f;
     }
     float clipv = 1.0f;
     uint32_t wmask = 0, cmask = 0;     // blocks written / clipped (uniform)
@@ -849,8 +939,11 @@ __device__ __forceinline__ void guarded_tile(const StepArgs& a, const MapLDS& M1
 #pragma unroll
                 for (int k = 0; k < NS; ++k) {
                     const float u = wave_max_nonneg(mcur[k]);
+                    float ru, cu;
+                    block_recip(u, ru, cu);
                     Av[k] = lane == qb ? u : Av[k];
-                    rv[k] = lane == qb ? ((u == 0.0f) ? 0.0f : 1.0f / u) : rv[k];
+                    rv[k] = lane == qb ? ru : rv[k];
+                    cv[k] = lane == qb ? cu : cv[k];
                     mcur[k] = 0.0f;
                 }
             }
@@ -894,10 +987,10 @@ __device__ __forceinline__ void guarded_tile(const StepArgs& a, const MapLDS& M1
             const int slot = Slot<OPT>::which(k);
             const int64_t eo = Slot<OPT>::elem_off(k, n);
             if constexpr (QUANT) {
-                const float rb = lane_value(rv[k], qb);
+                const float rb = lane_value(rv[k], qb), cb = lane_value(cv[k], qb);
                 uint32_t w = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w |= encode<FAST>(slot ? M2 : M1, st[k][i] * rb) << (8 * i);
+                for (int i = 0; i < 4; ++i) w |= encode<FAST>(slot ? M2 : M1, (st[k][i] * cb) * rb) << (8 * i);
                 store_code_word<VEC>(reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + eo, e, n, w);
             } else {
                 float* fp = reinterpret_cast<float*>(slot ? a.s2 : a.s1) + eo;

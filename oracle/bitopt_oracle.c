@@ -226,7 +226,11 @@ OREF_EXPORT void oref_nearest(const float* Q, const float* x, int64_t n, uint8_t
 
 /* Encode one block of fp32 values: absmax A = max |s| (exact), one correctly
  * rounded reciprocal r = 1/A per block (r = 0 when A = 0), then the nearest code
- * of s*r. */
+ * of s*r.  A subnormal A can have a reciprocal beyond the fp32 range; such a block
+ * is first scaled by 2^24 (exact): r = 1/(A*2^24) and the values (s*2^24)*r.
+ * Wherever 1/A is finite this gives the same bits as the plain form (a power of
+ * two commutes with rounding in the normal range), so the normalization stays
+ * invariant under power-of-two scaling of the block. */
 static float encode_block(const float* s, int len, const float* Q, uint8_t* codes)
 {
     float A = 0.0f;
@@ -234,9 +238,10 @@ static float encode_block(const float* s, int len, const float* Q, uint8_t* code
         float a = fabsf(s[i]);
         if (a > A) A = a;
     }
-    float r = (A == 0.0f) ? 0.0f : 1.0f / A;
+    float c = (A < 0x1p-126f) ? 0x1p24f : 1.0f;
+    float r = (A == 0.0f) ? 0.0f : 1.0f / (A * c);
     for (int i = 0; i < len; i++) {
-        float x = s[i] * r;
+        float x = (s[i] * c) * r;
         codes[i] = (uint8_t)nearest_code(Q, x);
     }
     return A;

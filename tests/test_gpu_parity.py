@@ -83,6 +83,28 @@ def test_step_8bit_max_unorm(name):
     _run(dict(OPTS[name], blocksize=256, max_unorm=0.002), RAGGED[256], "f32", 3, 300)
 
 
+def test_step_8bit_tiny_second_moments():
+    """Gradients so small that v = (1 - beta2) g^2 lands in (0, 2^-96) in some blocks:
+    those quads take the general square root, the rest the unscaled one."""
+    for name, dtype in (("adam", "f32"), ("ademamix", "bf16")):
+        n, B = RAGGED[256], 256
+        hp = dict(OPTS[name], blocksize=B)
+        p0 = W.to_dtype(W.normal_f32([970, 1], n, 0.02), dtype)
+        q = Quant8(hp, p0, dtype)
+        cmp = Compare()
+        for t in range(1, 4):
+            g = W.normal_f32([970, 2, t], n, 0.01)
+            scale = np.ones(n, np.float32)
+            for b in range(0, (n + B - 1) // B, 3):
+                scale[b * B:(b + 1) * B] = 1e-18          # g^2 ~ 1e-40, v ~ 1e-43
+            scale[5 * B + 7:5 * B + 40] = 1e-25             # tiny elements inside an ordinary block
+            g = W.to_dtype(g * scale, dtype)
+            q.step_gpu(t, to_dev(g, dtype))
+            q.step_oracle(t, g)
+            q.compare(cmp, f"{name} step {t}")
+        print(f"\n[tiny v {name} {dtype}] " + cmp.summary())
+
+
 def _jittered_map(signed, seed):
     """A sorted 256-entry map close to a standard one but equal to neither standard
     map, so the kernels take the binary-search encoder."""
@@ -229,6 +251,28 @@ def test_codec(dtype, bs):
                                                  "bf16": torch.bfloat16}[dtype])
         ref = oracle.dequantize_blockwise(codes_ref, absmax_ref, qmap, bs, dtype)
         np.testing.assert_array_equal(to_host(out, dtype), ref)
+
+
+@pytest.mark.parametrize("bs", [256, 2048])
+def test_codec_subnormal_blocks(bs):
+    """Blocks whose absmax is subnormal (plain reciprocal beyond fp32 range) next to
+    ordinary ones: the prescaled normalization on both sides."""
+    for signed in (True, False):
+        n = RAGGED[bs]
+        x = W.normal_f32([910, bs], n, 0.01)
+        if not signed:
+            x = np.abs(x)
+        nb = (n + bs - 1) // bs
+        for b in range(0, nb, 2):
+            x[b * bs:(b + 1) * bs] *= np.float32(2.0 ** -128)
+        qmap = oracle.dynamic_map(signed)
+        codes_ref, absmax_ref = oracle.quantize_blockwise(x, "f32", qmap, bs)
+        assert np.any((absmax_ref > 0) & (absmax_ref < 2.0 ** -126))
+        codes, absmax = bitopt.quantize_blockwise(to_dev(x, "f32"), bitopt.create_dynamic_map(signed).cuda(), bs)
+        cmp = Compare()
+        cmp.codes(to_host(codes), codes_ref, "codes")
+        cmp.values(to_host(absmax), absmax_ref, 1e-6, "absmax", kind="a")
+        assert cmp.bit_exact, cmp.summary()
 
 
 def test_codec_unaligned_and_empty():

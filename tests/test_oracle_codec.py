@@ -121,6 +121,26 @@ def test_quantize_zero_block(oref):
         assert absmax[1] == 0.5 and np.all(codes[256:] == 255)
 
 
+@pytest.mark.parametrize("signed", [True, False])
+def test_quantize_invariant_under_power_of_two_scaling(oref, signed):
+    """Scaling a block by a power of two (exactly, no bits lost) scales its absmax by
+    the same power and leaves its codes unchanged -- down into the subnormal range,
+    where the plain reciprocal of the absmax would overflow."""
+    q = oref.dynamic_map(signed)
+    rng = np.random.default_rng(5)
+    n = 4 * 256
+    ints = rng.integers(-1024 if signed else 0, 1025, n).astype(np.float32)
+    ints[::97] = 0.0
+    x = ints / np.float32(1024.0)                      # 11 significant bits, |x| <= 1
+    codes, absmax = oref.quantize_blockwise(x, "f32", q, 256)
+    for k in (10, 60, 100, 126, 127, 128, 130, 134, 138):
+        xs = (x.astype(np.float64) * 2.0 ** -k).astype(np.float32)
+        assert np.array_equal(xs.astype(np.float64) * 2.0 ** k, x.astype(np.float64))   # exact
+        c2, a2 = oref.quantize_blockwise(xs, "f32", q, 256)
+        np.testing.assert_array_equal(a2.astype(np.float64), absmax.astype(np.float64) * 2.0 ** -k)
+        np.testing.assert_array_equal(c2, codes, err_msg=f"2^-{k}")
+
+
 def test_fp16_rounding_matches_numpy(oref):
     rng = np.random.default_rng(11)
     specials = np.float32([0.0, -0.0, 65504.0, 65519.996, 65520.0, 1e6, -1e6, 6.0e-8, 2.98e-8,
