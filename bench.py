@@ -254,7 +254,9 @@ def _rocprof(args, outdir, extra, env=None):
     r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=300)
     if r.returncode != 0:
         raise SystemExit(f"rocprofv3 failed ({r.returncode}): {' '.join(cmd)}")
-    return " ".join(cmd)
+    # as recorded: the repository root as <repo>, the interpreter as python
+    shown = ["python" if c == sys.executable else c.replace(ROOT, "<repo>") for c in cmd]
+    return " ".join(shown)
 
 
 def _csv_rows(outdir, suffix):
@@ -330,7 +332,9 @@ def profile(workload: str, outdir: str, steps: int):
         f.write(f"| HBM traffic per launch (scaled) | {(fetch_b + write_b) / 1e6:.1f} MB "
                 f"({(fetch_b + write_b) / alg:.3f} x algorithmic) |\n")
         f.write(f"| library source hash | {source_hash()} |\n\n")
-        f.write("Commands (run from /tmp, TMPDIR=/tmp; raw output in the -d directories):\n\n")
+        f.write(f"Made by `python bench.py --profile <outdir> --workload {workload} --profile-steps {steps}` "
+                "(from the repository root), which runs the three profiler passes below from /tmp with "
+                "TMPDIR=/tmp; raw output stays in the -d directories.\n\n")
         for k, c in cmds.items():
             f.write(f"- {k}: `{c}`\n")
     print(json.dumps(d))

@@ -586,7 +586,15 @@ struct TileRaw {
     uint32_t code[QUANT ? NS : 1][NQ];
     f32x4 fst[QUANT ? 1 : NS][NQ];
     float A[NS][BPT];
+    uint32_t live;      // skip_zeros: bit b set when block b has a nonzero gradient (uniform)
 };
+
+// Whether a raw gradient word holds a nonzero value (-0 counts as zero): one fp32
+// value, or two 16-bit ones.
+template <int DT> __device__ __forceinline__ bool word_nonzero(uint32_t w) {
+    if constexpr (DT == kF32) return (w & 0x7fffffffu) != 0u;
+    else return (w & 0x7fff7fffu) != 0u;
+}
 
 template <int DT, int PW>
 __device__ __forceinline__ void widen_words(const uint32_t (&w)[PW], float v[4]) {
@@ -605,9 +613,40 @@ __device__ __forceinline__ bool tile_full(const StepArgs& a, int64_t t) {
     return a.vec && (t + 1) * Layout<BS>::TE <= a.n;
 }
 
-// Issue every load of one full tile (vector accesses).
-template <int DT, int OPT, int BS, bool QUANT>
-__device__ __forceinline__ void load_tile(const StepArgs& a, int64_t base, int lane,
+// The loads of one full tile (vector accesses), in two parts.  load_grad reads the
+// gradient and, with skip_zeros, marks the blocks holding a nonzero gradient;
+// load_rest reads the other inputs -- with skip_zeros only for those blocks (an
+// all-zero block is neither read nor written).
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
+__device__ __forceinline__ void load_grad(const StepArgs& a, int64_t base, int lane,
+                                          TileRaw<DT, OPT, BS, QUANT>& r) {
+    using L = Layout<BS>;
+    using R = TileRaw<DT, OPT, BS, QUANT>;
+    using Raw4 = typename Elem<DT>::Raw4;
+    using T = typename Elem<DT>::T;
+#pragma unroll
+    for (int q = 0; q < R::NQ; ++q) {
+        const Raw4 gv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const T*>(a.g) + L::elem(base, lane, q)));
+#pragma unroll
+        for (int i = 0; i < R::PW; ++i) r.g[q][i] = gv[i];
+    }
+    r.live = (1u << R::BPT) - 1u;
+    if constexpr (SKIP) {
+        r.live = 0;
+#pragma unroll
+        for (int b = 0; b < R::BPT; ++b) {
+            bool nz = false;
+#pragma unroll
+            for (int qq = 0; qq < L::QPB; ++qq)
+#pragma unroll
+                for (int i = 0; i < R::PW; ++i) nz = nz || word_nonzero<DT>(r.g[b * L::QPB + qq][i]);
+            if (wave_any(nz)) r.live |= 1u << b;
+        }
+    }
+}
+
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
+__device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int lane,
                                           TileRaw<DT, OPT, BS, QUANT>& r) {
     using L = Layout<BS>;
     using R = TileRaw<DT, OPT, BS, QUANT>;
@@ -616,11 +655,10 @@ __device__ __forceinline__ void load_tile(const StepArgs& a, int64_t base, int l
     const int64_t blk0 = base / BS;
 #pragma unroll
     for (int q = 0; q < R::NQ; ++q) {
-        const int64_t e = L::elem(base, lane, q);
-        const Raw4 pv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const T*>(a.p) + e));
-        const Raw4 gv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const T*>(a.g) + e));
+        if (SKIP && !((r.live >> (q / L::QPB)) & 1u)) continue;          // wave-uniform
+        const Raw4 pv = ld_stream(reinterpret_cast<const Raw4*>(reinterpret_cast<const T*>(a.p) + L::elem(base, lane, q)));
 #pragma unroll
-        for (int i = 0; i < R::PW; ++i) { r.p[q][i] = pv[i]; r.g[q][i] = gv[i]; }
+        for (int i = 0; i < R::PW; ++i) r.p[q][i] = pv[i];
     }
 #pragma unroll
     for (int k = 0; k < R::NS; ++k) {
@@ -629,20 +667,32 @@ __device__ __forceinline__ void load_tile(const StepArgs& a, int64_t base, int l
         if constexpr (QUANT) {
             const uint8_t* cp = reinterpret_cast<const uint8_t*>(slot ? a.s2 : a.s1) + eo;
 #pragma unroll
-            for (int q = 0; q < R::NQ; ++q)
+            for (int q = 0; q < R::NQ; ++q) {
+                if (SKIP && !((r.live >> (q / L::QPB)) & 1u)) continue;
                 r.code[k][q] = ld_stream(reinterpret_cast<const uint32_t*>(cp + L::elem(base, lane, q)));
+            }
             const float* am = (slot ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
 #pragma unroll
-            for (int b = 0; b < R::BPT; ++b) r.A[k][b] = gbl(am)[blk0 + b];
+            for (int b = 0; b < R::BPT; ++b)
+                r.A[k][b] = (!SKIP || ((r.live >> b) & 1u)) ? gbl(am)[blk0 + b] : 0.0f;
         } else {
             const float* fp = reinterpret_cast<const float*>(slot ? a.s2 : a.s1) + eo;
 #pragma unroll
-            for (int q = 0; q < R::NQ; ++q)
+            for (int q = 0; q < R::NQ; ++q) {
+                if (SKIP && !((r.live >> (q / L::QPB)) & 1u)) continue;
                 r.fst[k][q] = ld_stream(reinterpret_cast<const f32x4*>(fp + L::elem(base, lane, q)));
+            }
 #pragma unroll
             for (int b = 0; b < R::BPT; ++b) r.A[k][b] = 0.0f;
         }
     }
+}
+
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
+__device__ __forceinline__ void load_tile(const StepArgs& a, int64_t base, int lane,
+                                          TileRaw<DT, OPT, BS, QUANT>& r) {
+    load_grad<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
+    load_rest<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
 }
 
 // Compute and store one full tile from its raw inputs.
@@ -665,6 +715,18 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
 
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
+        if (SKIP && !((r.live >> (q / QPB)) & 1u)) {
+            // a block without a nonzero gradient: nothing was read, nothing is written
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pf[q][i] = 0.0f;
+                dl[q][i] = 0.0f;
+                live[q][i] = false;
+#pragma unroll
+                for (int k = 0; k < NS; ++k) st[k][q][i] = 0.0f;
+            }
+            continue;
+        }
         float gq[4];
         widen_words<DT>(r.p[q], pf[q]);
         widen_words<DT>(r.g[q], gq);
@@ -1067,7 +1129,7 @@ __device__ __forceinline__ void step_tiles(const StepArgs& a0, const MapLDS& M1,
         if (tile_full<BS>(a, t)) {
             if constexpr (WHOLE) {
                 TileRaw<DT, OPT, BS, QUANT> x;
-                load_tile<DT, OPT, BS, QUANT>(a, t * TE, lane, x);
+                load_tile<DT, OPT, BS, QUANT, SKIP>(a, t * TE, lane, x);
                 process_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST>(a, M1, M2, t * TE, lane, x);
             } else {
                 guarded_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST, true>(a, M1, M2, t * TE, lane);
@@ -1075,6 +1137,42 @@ __device__ __forceinline__ void step_tiles(const StepArgs& a0, const MapLDS& M1,
         } else {
             guarded_tile<DT, OPT, BS, QUANT, SKIP, UNORM, FAST, false>(a, M1, M2, t * TE, lane);
         }
+    }
+}
+
+// skip_zeros, one tile per wave (single tensor, grid covering every tile): the
+// gradient is read before the maps are staged, and a group none of whose tiles has
+// a nonzero gradient ends there -- most groups of a sparse update do no more than
+// read their gradients.
+template <int DT, int OPT, int BS, bool QUANT, bool UNORM, int NMAPS>
+__device__ __forceinline__ void step_one_tile_skip(const StepArgs& a, float* Q1, float* Q2, float* T1, float* T2,
+                                                   uint8_t* B1, uint8_t* B2, uint32_t* vote) {
+    constexpr int64_t TE = Layout<BS>::TE;
+    const int lane = threadIdx.x & 63;
+    const int64_t t = wave_id();
+    const int64_t ntiles = total_tiles<BS, false>(a);
+    const bool full = t < ntiles && tile_full<BS>(a, t);
+    TileRaw<DT, OPT, BS, QUANT> x;
+    x.live = 0;
+    if (full) load_grad<DT, OPT, BS, QUANT, true>(a, t * TE, lane, x);
+    // ragged or misaligned tiles are taken as having work
+    const bool work = full ? x.live != 0u : t < ntiles;
+    if (!__syncthreads_or(work)) return;
+    const MapLDS M1{Q1, T1, B1}, M2{Q2, T2, B2};
+    bool fast = true;
+    if constexpr (QUANT) fast = stage_maps<NMAPS>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote);
+    if (!work) return;
+    if (full) {
+        if (!QUANT || fast) {
+            load_rest<DT, OPT, BS, QUANT, true>(a, t * TE, lane, x);
+            process_tile<DT, OPT, BS, QUANT, true, UNORM, true>(a, M1, M2, t * TE, lane, x);
+        } else {
+            guarded_tile<DT, OPT, BS, QUANT, true, UNORM, false, true>(a, M1, M2, t * TE, lane);
+        }
+    } else if (fast) {
+        guarded_tile<DT, OPT, BS, QUANT, true, UNORM, true, false>(a, M1, M2, t * TE, lane);
+    } else {
+        guarded_tile<DT, OPT, BS, QUANT, true, UNORM, false, false>(a, M1, M2, t * TE, lane);
     }
 }
 
@@ -1093,6 +1191,12 @@ __global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
         const BITOPT_CONSTANT TensorDesc* tab = (const BITOPT_CONSTANT TensorDesc*)a.table;
         for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = tab[i].tile0;
         __syncthreads();
+    }
+    if constexpr (SKIP && !MULTI) {
+        if ((int64_t)gridDim.x * kWavesPerGroup >= total_tiles<BS, false>(a)) {     // uniform
+            step_one_tile_skip<DT, OPT, BS, QUANT, UNORM, NMAPS>(a, Q1, Q2, T1, T2, B1, B2, vote);
+            return;
+        }
     }
     if constexpr (QUANT) {
         if (stage_maps<NMAPS>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote))
