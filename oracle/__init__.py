@@ -16,8 +16,10 @@ import numpy as np
 from . import build as _build
 
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
-OPTIMIZERS = {"adam": 0, "adamw": 0, "ademamix": 1, "momentum": 2, "lion": 3}
-NUM_STATES = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1}
+OPTIMIZERS = {"adam": 0, "adamw": 0, "ademamix": 1, "momentum": 2, "lion": 3, "rmsprop": 4, "adagrad": 5}
+NUM_STATES = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1, "rmsprop": 1, "adagrad": 1}
+# optimizers whose single state is non-negative (encoded with the unsigned map)
+UNSIGNED_STATE1 = ("rmsprop", "adagrad")
 
 
 class _HParams(ctypes.Structure):

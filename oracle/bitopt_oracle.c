@@ -41,7 +41,7 @@
 #define OREF_EXPORT __attribute__((visibility("default")))
 
 enum { OREF_F32 = 0, OREF_F16 = 1, OREF_BF16 = 2 };
-enum { OREF_ADAM = 0, OREF_ADEMAMIX = 1, OREF_MOMENTUM = 2, OREF_LION = 3 };
+enum { OREF_ADAM = 0, OREF_ADEMAMIX = 1, OREF_MOMENTUM = 2, OREF_LION = 3, OREF_RMSPROP = 4, OREF_ADAGRAD = 5 };
 enum { OREF_MAXB = 4096 };
 
 /* Hyper-parameters of one step call; field meanings follow [P2] Optimizer2State /
@@ -341,6 +341,9 @@ OREF_EXPORT void oref_step_scalars(const oref_hparams* h, int32_t t, float* out1
 /*                s2 = nu (unsigned map)                                         */
 /*   Momentum   : s1 = momentum_buffer (signed map)                              */
 /*   Lion       : s1 = exp_avg (signed map)                                      */
+/*   RMSprop    : s1 = square_avg (non-negative: the unsigned map)               */
+/*   Adagrad    : s1 = sum of squared gradients (unsigned map)                   */
+/* (the maps are the caller's; these are the ones the tests hand in)              */
 /* ------------------------------------------------------------------------- */
 
 typedef struct {
@@ -445,6 +448,35 @@ static void step_block(const oref_hparams* h, const step_scalars* sc, int64_t b,
             st[0][i] = buf;
             break;
         }
+        case OREF_RMSPROP: {
+            /* [P1] optimizer table: RMSprop8bit(p, 0.01, 0.9) against torch.optim.RMSprop
+             * (lr 0.01, alpha 0.9): square_avg = alpha*square_avg + (1-alpha)*g'^2,
+             * p -= lr * g'/(sqrt(square_avg) + eps), g' = g + wd*p (decay folded in). */
+            float v = st[0][i];
+            t1 = sc->wd * pi; float g2 = gi + t1;
+            float gg = g2 * g2;
+            t1 = sc->b1 * v; t2 = sc->omb1 * gg; v = t1 + t2;
+            float d = sqrtf(v);
+            d = d + sc->eps;
+            float u = g2 / d;
+            dv[i] = sc->lr * u;
+            st[0][i] = v;
+            break;
+        }
+        case OREF_ADAGRAD: {
+            /* [P2]: the 1-state example.  torch.optim.Adagrad (no lr decay, zero initial
+             * accumulator): sum += g'^2, p -= lr * g'/(sqrt(sum) + eps), g' = g + wd*p. */
+            float v = st[0][i];
+            t1 = sc->wd * pi; float g2 = gi + t1;
+            float gg = g2 * g2;
+            v = v + gg;
+            float d = sqrtf(v);
+            d = d + sc->eps;
+            float u = g2 / d;
+            dv[i] = sc->lr * u;
+            st[0][i] = v;
+            break;
+        }
         default: { /* Lion */
             float m = st[0][i];
             t1 = sc->b1 * m; t2 = sc->omb1 * gi;
@@ -479,7 +511,7 @@ static void step_block(const oref_hparams* h, const step_scalars* sc, int64_t b,
         float d = dv[i];
         if (clipped) d = d * clip;
         float pn;
-        if (opt == OREF_MOMENTUM) pn = pv[i] - d;
+        if (opt == OREF_MOMENTUM || opt == OREF_RMSPROP || opt == OREF_ADAGRAD) pn = pv[i] - d;   /* coupled decay */
         else { float pd = pv[i] * sc->decay; pn = pd - d; }
         store_elem(p, dtype, off + i, pn);
     }
@@ -499,7 +531,7 @@ static void step_block(const oref_hparams* h, const step_scalars* sc, int64_t b,
 static int check_hparams(const oref_hparams* h, int32_t step, int64_t n)
 {
     if (!h || step < 1 || n < 0) return -1;
-    if (h->optimizer < OREF_ADAM || h->optimizer > OREF_LION) return -1;
+    if (h->optimizer < OREF_ADAM || h->optimizer > OREF_ADAGRAD) return -1;
     if (h->blocksize < 1 || h->blocksize > OREF_MAXB) return -1;
     return 0;
 }

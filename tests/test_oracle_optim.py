@@ -4,15 +4,16 @@ Pages:
   "optim_overview" (Optimizer2State / Optimizer1State hyper-parameters: lr, betas,
     eps, weight_decay, max_unorm, skip_zeros, alpha, t_alpha, t_beta3);
   "[XPU] Implemented 8bit optimizers in triton #1692" (optimizer table: the 8-bit
-    optimizers are checked against torch.optim.Adam / AdamW / SGD(p, 0.01, 0.9), a
-    Lion implementation and a reference AdEMAMix; test body: 50-step tracking
-    protocol with re-sync and its tolerances);
+    optimizers are checked against torch.optim.Adam / AdamW / SGD(p, 0.01, 0.9) /
+    RMSprop(p, 0.01, 0.9), a Lion implementation and a reference AdEMAMix; test
+    body: 50-step tracking protocol with re-sync and its tolerances);
   "Support skip_zeros in the XPU Triton optimizer kernels #2097" (description and
     Tests: zero-gradient elements untouched, the rest identical to skip_zeros=False;
     zero test on the raw gradient; default path unchanged).
 
 What pins what:
-  * 32-bit mode (identity codec) vs torch.optim.AdamW / SGD run in float64, and vs
+  * 32-bit mode (identity codec) vs torch.optim.AdamW / SGD / RMSprop / Adagrad run
+    in float64, and vs
     float64 statements of Lion and AdEMAMix written in their papers' form (bias-
     corrected moments, decoupled decay term inside the step), over 10 steps.
   * Closed forms at t = 1 from a zero state.
@@ -70,7 +71,7 @@ def _new8(oref, hp, n):
     opt = hp["optimizer"]
     st = dict(state1=np.zeros(2 * n if opt == "ademamix" else n, np.uint8),
               absmax1=np.zeros(2 * nb if opt == "ademamix" else nb, f32),
-              qmap1=oref.dynamic_map(True))
+              qmap1=oref.dynamic_map(opt not in oref.UNSIGNED_STATE1))
     if oref.NUM_STATES[opt] >= 2:
         st.update(state2=np.zeros(n, np.uint8), absmax2=np.zeros(nb, f32), qmap2=oref.dynamic_map(False))
     return st
@@ -113,6 +114,26 @@ def test_momentum_32bit_matches_torch_sgd_fp64(oref):
                                                       weight_decay=_f(0.01), foreach=False), p0, gs)
     np.testing.assert_allclose(p, ref_p, rtol=1e-6, atol=1e-8)
     _close(buf, st["momentum_buffer"].numpy())
+
+
+def test_rmsprop_32bit_matches_torch_fp64(oref):
+    p0, gs = _inputs(3000, 10, 23)
+    hp = dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8, weight_decay=0.01)
+    p, sq, _ = _run32(oref, hp, p0, gs)
+    ref_p, st = _torch64(lambda ps: torch.optim.RMSprop(ps, lr=_f(0.01), alpha=_f(0.9), eps=_f(1e-8),
+                                                          weight_decay=_f(0.01), foreach=False), p0, gs)
+    np.testing.assert_allclose(p, ref_p, rtol=1e-6, atol=1e-8)
+    _close(sq, st["square_avg"].numpy())
+
+
+def test_adagrad_32bit_matches_torch_fp64(oref):
+    p0, gs = _inputs(3000, 10, 24)
+    hp = dict(optimizer="adagrad", lr=0.01, eps=1e-10, weight_decay=0.01)
+    p, acc, _ = _run32(oref, hp, p0, gs)
+    ref_p, st = _torch64(lambda ps: torch.optim.Adagrad(ps, lr=_f(0.01), eps=_f(1e-10), weight_decay=_f(0.01),
+                                                          foreach=False), p0, gs)
+    np.testing.assert_allclose(p, ref_p, rtol=1e-6, atol=1e-8)
+    _close(acc, st["sum"].numpy())
 
 
 def _lion64(p0, gs, lr, b1, b2, wd):
@@ -237,6 +258,26 @@ def test_first_step_closed_forms(oref):
         b3 = oref.beta3_schedule(_f(0.9), _f(0.9999), 1, 100)
         expect = p0 - 1e-3 * (g + 0.05 * (1 - b3) * g) / (np.abs(g) + 1e-8)
         np.testing.assert_allclose(p, expect, rtol=2e-6, atol=1e-9)
+        # RMSprop: square_avg = (1-alpha) g'^2, step = lr g'/(sqrt(1-alpha)|g'| + eps), g' = g + wd p
+        hp = dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8, weight_decay=0.01)
+        p = p0.copy()
+        if mode == "32":
+            oref.step_32bit(hp, 1, p, g, "f32", np.zeros(n, f32))
+        else:
+            _step8(oref, hp, 1, p, g, "f32", _new8(oref, hp, n))
+        # (steps of ~0.03 on parameters of ~0.02: a few fp32 ulps of 0.03 absolute)
+        g2 = g.astype(np.float64) + 0.01 * p0
+        expect = p0 - 0.01 * g2 / (np.sqrt(0.1) * np.abs(g2) + 1e-8)
+        np.testing.assert_allclose(p, expect, rtol=2e-6, atol=2e-8)
+        # Adagrad: sum = g'^2, step = lr g'/(|g'| + eps) = lr sign(g') up to eps
+        hp = dict(optimizer="adagrad", lr=0.01, eps=1e-10, weight_decay=0.01)
+        p = p0.copy()
+        if mode == "32":
+            oref.step_32bit(hp, 1, p, g, "f32", np.zeros(n, f32))
+        else:
+            _step8(oref, hp, 1, p, g, "f32", _new8(oref, hp, n))
+        expect = p0 - 0.01 * g2 / (np.abs(g2) + 1e-10)
+        np.testing.assert_allclose(p, expect, rtol=2e-6, atol=2e-8)
 
 
 # ----------------------------------------------------------------------------- AdEMAMix(alpha=0) == Adam
@@ -267,6 +308,10 @@ def _ref32_torch(name):
         return lambda ps: torch.optim.Adam(ps, lr=_f(1e-3), betas=(_f(0.9), _f(0.999)), eps=_f(1e-8))
     if name == "momentum":
         return lambda ps: torch.optim.SGD(ps, lr=_f(0.01), momentum=_f(0.9))
+    if name == "rmsprop":
+        return lambda ps: torch.optim.RMSprop(ps, lr=_f(0.01), alpha=_f(0.9))
+    if name == "adagrad":
+        return lambda ps: torch.optim.Adagrad(ps, lr=_f(0.01), eps=_f(1e-10))
     return None
 
 
@@ -310,6 +355,10 @@ class _Ref32:
             return [s["exp_avg"], s["exp_avg_sq"]]
         if self.name == "momentum":
             return [self.opt.state[self.p]["momentum_buffer"]]
+        if self.name == "rmsprop":
+            return [self.opt.state[self.p]["square_avg"]]
+        if self.name == "adagrad":
+            return [self.opt.state[self.p]["sum"]]
         if self.name == "lion":
             return [self.m]
         return [self.m1, self.m2, self.nu]
@@ -320,7 +369,8 @@ class _Ref32:
 
 
 @pytest.mark.parametrize("name,dtype", [("adam", "f32"), ("adam", "f16"), ("momentum", "f32"),
-                                        ("lion", "f32"), ("ademamix", "bf16")])
+                                        ("lion", "f32"), ("ademamix", "bf16"), ("rmsprop", "f32"),
+                                        ("adagrad", "f32")])
 def test_8bit_tracks_32bit_with_resync(oref, name, dtype):
     tol = json.load(open(os.path.join(GOLDEN, "p1_tracking_tolerances.json")))
     pt = tol["param"][dtype]
@@ -330,7 +380,9 @@ def test_8bit_tracks_32bit_with_resync(oref, name, dtype):
     hp = {"adam": dict(optimizer="adam", lr=1e-3),
           "momentum": dict(optimizer="momentum", lr=0.01, beta1=0.9),
           "lion": dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99),
-          "ademamix": dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0)}[name]
+          "ademamix": dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0),
+          "rmsprop": dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8),
+          "adagrad": dict(optimizer="adagrad", lr=0.01, eps=1e-10)}[name]
     hp["blocksize"] = B
     steps = tol["steps"] if name == "adam" and dtype == "f32" else 20
     p8 = W.to_dtype(W.normal_f32([77, 1], n, tol["param_scale"]), dtype)
@@ -390,6 +442,8 @@ OPT_HP = {
                      weight_decay=0.01),
     "momentum": dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01),
     "lion": dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01),
+    "rmsprop": dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8, weight_decay=0.01),
+    "adagrad": dict(optimizer="adagrad", lr=0.01, eps=1e-10, weight_decay=0.01),
 }
 
 
@@ -470,7 +524,7 @@ def test_skip_zeros_32bit_states_untouched(oref, name):
 
 # ----------------------------------------------------------------------------- max_unorm
 
-@pytest.mark.parametrize("name", ["adam", "momentum", "lion", "ademamix"])
+@pytest.mark.parametrize("name", ["adam", "momentum", "lion", "ademamix", "rmsprop", "adagrad"])
 def test_max_unorm(oref, name):
     n, B = 256 * 12 + 5, 256
     hp = dict(OPT_HP[name], blocksize=B, weight_decay=0.0)
