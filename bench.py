@@ -47,6 +47,10 @@ def workload_by_name(name):
         "momentum_fp16_skip1": lambda: W.c4_embedding("momentum", True),
         "lion_fp16_skip0": lambda: W.c4_embedding("lion", False),
         "lion_fp16_skip1": lambda: W.c4_embedding("lion", True),
+        "rmsprop_fp32_b256": lambda: W.f2_one_state_4096("rmsprop", "f32"),
+        "rmsprop_bf16_b256": lambda: W.f2_one_state_4096("rmsprop", "bf16"),
+        "adagrad_fp32_b256": lambda: W.f2_one_state_4096("adagrad", "f32"),
+        "adagrad_bf16_b256": lambda: W.f2_one_state_4096("adagrad", "bf16"),
         "adam_fp32_256x256": W.c1_adam_256,
         "gpt_1p3b": W.c5_gpt_1p3b,
     }
@@ -55,7 +59,7 @@ def workload_by_name(name):
 
 def workload_bytes(wl) -> float:
     """Algorithmic HBM bytes of one step over every tensor of the workload."""
-    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1}[wl.hp["optimizer"]]
+    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1, "rmsprop": 1, "adagrad": 1}[wl.hp["optimizer"]]
     total = 0.0
     for t in wl.tensors:
         if t.eightbit:
@@ -306,7 +310,7 @@ def profile(workload: str, outdir: str, steps: int):
     write_b = sum(ws) / len(ws) * w_scale * 1024.0
     wl = workload_by_name(workload)
     t = wl.tensors[0]
-    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1}[wl.hp["optimizer"]]
+    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1, "rmsprop": 1, "adagrad": 1}[wl.hp["optimizer"]]
     alg = W.bytes_per_element(t.dtype, ns, wl.hp["blocksize"]) * t.numel
     d = {"workload": workload, "kernel": kname, "source_hash": source_hash(),
          "kernel_trace_calls": calls, "kernel_trace_avg_us": avg_ns / 1e3,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitopt.s
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE = 0, -1, -2, -3
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-OPTIMIZERS = {"adam": 0, "adamw": 0, "ademamix": 1, "momentum": 2, "lion": 3}
+OPTIMIZERS = {"adam": 0, "adamw": 0, "ademamix": 1, "momentum": 2, "lion": 3, "rmsprop": 4, "adagrad": 5}
 TWO_STATE = ("adam", "adamw", "ademamix")
 SCALAR_NAMES = ["lr", "b1", "b2", "eps", "wd", "omb1", "omb2", "ic1", "rs2", "decay",
                 "b3t", "omb3", "alpha_t", "max_unorm"]

@@ -47,7 +47,7 @@ bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; }
 // Hyper-parameter checks shared by every step entry point.
 int check_hparams(const bitopt_hparams* hp, int32_t step, int64_t n, const char* fn) {
     if (!hp) return fail(BITOPT_ERR_INVALID_ARG, "%s: hp is NULL", fn);
-    if (hp->optimizer < BITOPT_ADAM || hp->optimizer > BITOPT_LION)
+    if (hp->optimizer < BITOPT_ADAM || hp->optimizer > BITOPT_ADAGRAD)
         return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown optimizer %d", fn, hp->optimizer);
     if (step < 1) return fail(BITOPT_ERR_INVALID_ARG, "%s: step must be >= 1 (got %d)", fn, step);
     if (n < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: n < 0", fn);
@@ -138,6 +138,8 @@ hipError_t dispatch_step(const bitopt::StepArgs& a, int opt, int dtype, int bs, 
     case BITOPT_ADAM: return bitopt::launch_step_adam(a, dtype, bs, quant, skip, unorm, s);
     case BITOPT_ADEMAMIX: return bitopt::launch_step_ademamix(a, dtype, bs, quant, skip, unorm, s);
     case BITOPT_MOMENTUM: return bitopt::launch_step_momentum(a, dtype, bs, quant, skip, unorm, s);
+    case BITOPT_RMSPROP: return bitopt::launch_step_rmsprop(a, dtype, bs, quant, skip, unorm, s);
+    case BITOPT_ADAGRAD: return bitopt::launch_step_adagrad(a, dtype, bs, quant, skip, unorm, s);
     default: return bitopt::launch_step_lion(a, dtype, bs, quant, skip, unorm, s);
     }
 }
@@ -242,7 +244,8 @@ int bitopt_step_8bit_blockwise_1state(const bitopt_hparams* hp, int32_t step, vo
                                       const float* qmap1, void* stream) {
     const char* fn = "bitopt_step_8bit_blockwise_1state";
     if (int rc = check_hparams(hp, step, n, fn)) return rc;
-    if (hp->optimizer != BITOPT_MOMENTUM && hp->optimizer != BITOPT_LION)
+    if (hp->optimizer != BITOPT_MOMENTUM && hp->optimizer != BITOPT_LION && hp->optimizer != BITOPT_RMSPROP &&
+        hp->optimizer != BITOPT_ADAGRAD)
         return fail(BITOPT_ERR_INVALID_ARG, "%s: optimizer %d is not a 1-state optimizer", fn, hp->optimizer);
     if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (n == 0) return ok();
@@ -266,7 +269,8 @@ int bitopt_step_32bit_1state(const bitopt_hparams* hp, int32_t step, void* p, co
                              int64_t n, float* state1, void* stream) {
     const char* fn = "bitopt_step_32bit_1state";
     if (int rc = check_hparams(hp, step, n, fn)) return rc;
-    if (hp->optimizer != BITOPT_MOMENTUM && hp->optimizer != BITOPT_LION)
+    if (hp->optimizer != BITOPT_MOMENTUM && hp->optimizer != BITOPT_LION && hp->optimizer != BITOPT_RMSPROP &&
+        hp->optimizer != BITOPT_ADAGRAD)
         return fail(BITOPT_ERR_INVALID_ARG, "%s: optimizer %d is not a 1-state optimizer", fn, hp->optimizer);
     if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (n == 0) return ok();

@@ -32,7 +32,7 @@
 namespace bitopt {
 
 constexpr int kF32 = 0, kF16 = 1, kBF16 = 2;
-constexpr int kAdam = 0, kAdemamix = 1, kMomentum = 2, kLion = 3;
+constexpr int kAdam = 0, kAdemamix = 1, kMomentum = 2, kLion = 3, kRmsprop = 4, kAdagrad = 5;
 constexpr int kThreads = 256;              // 4 waves per workgroup
 constexpr int kWavesPerGroup = kThreads / 64;
 
@@ -80,6 +80,8 @@ struct StepArgs {
 };
 
 template <int OPT> struct NumStates { static constexpr int v = OPT == kAdemamix ? 3 : (OPT == kAdam ? 2 : 1); };
+// 1-state optimizers whose state is never negative: their map is expected to be the unsigned one.
+template <int OPT> struct UnsignedState1 { static constexpr int v = (OPT == kRmsprop || OPT == kAdagrad) ? 1 : 0; };
 
 // ---------------------------------------------------------------- number formats
 
@@ -276,13 +278,14 @@ __device__ __forceinline__ uint32_t encode(const MapLDS& m, float x) {
 }
 
 // Stage up to two codebooks into LDS.  Map 1 is expected to be the standard signed
-// map and map 2 the standard unsigned one, so their search tables are fetched
+// map (EXP1 = 1: the unsigned one) and map 2 the standard unsigned one, so their
+// search tables are fetched
 // together with the maps (one round of loads, one barrier).  Each wave votes on
 // which standard map each staged map equals; if the group's vote shows the
 // standard maps in the other assignment, the tables are staged again.  Returns
 // whether the table encoder applies (uniform over the group); otherwise the
 // caller uses the binary search over the staged maps.
-template <int NMAPS>
+template <int NMAPS, int EXP1 = 0>
 __device__ __forceinline__ bool stage_maps(const float* q1, const float* q2, float* Q1, float* Q2,
                                            float* T1, float* T2, uint8_t* B1, uint8_t* B2, uint32_t* vote) {
     constexpr int NV = search::kNB / 16;                 // 16-byte words per bucket table
@@ -295,10 +298,11 @@ __device__ __forceinline__ bool stage_maps(const float* q1, const float* q2, flo
     const uint32_t v1 = __float_as_uint(gbl(q1)[tid]);
     const uint32_t v2 = NMAPS > 1 ? __float_as_uint(gbl(q2)[tid]) : 0u;
     const uint32_t s0 = kStdQ0[tid], s1 = kStdQ1[tid];
-    const uint32_t t1 = kStdTau0[tid];
+    const uint32_t t1 = EXP1 ? kStdTau1[tid] : kStdTau0[tid];
     const uint32_t t2 = NMAPS > 1 ? kStdTau1[tid] : 0u;
-    const u32x4 b1a = bs[tid];
-    const u32x4 b1b = two ? bs[tid + kThreads] : u32x4{0u, 0u, 0u, 0u};
+    const u32x4* b1src = EXP1 ? bu : bs;
+    const u32x4 b1a = b1src[tid];
+    const u32x4 b1b = two ? b1src[tid + kThreads] : u32x4{0u, 0u, 0u, 0u};
     u32x4 b2a = {0u, 0u, 0u, 0u}, b2b = {0u, 0u, 0u, 0u};
     if constexpr (NMAPS > 1) {
         b2a = bu[tid];
@@ -327,7 +331,7 @@ __device__ __forceinline__ bool stage_maps(const float* q1, const float* q2, flo
     uint32_t all = vote[0];
 #pragma unroll
     for (int w = 1; w < kWavesPerGroup; ++w) all &= vote[w];
-    if ((all & 1u) && (NMAPS == 1 || (all & 8u))) return true;
+    if ((all & (EXP1 ? 2u : 1u)) && (NMAPS == 1 || (all & 8u))) return true;
     const int w1 = (all & 1u) ? 0 : (all & 2u) ? 1 : -1;
     const int w2 = NMAPS == 1 ? 0 : (all & 4u) ? 0 : (all & 8u) ? 1 : -1;
     if (w1 < 0 || w2 < 0) return false;
@@ -369,55 +373,79 @@ __device__ __forceinline__ bool sqrt_needs_scaling(float v) {
     return __float_as_uint(v) - 1u < 0x0F7FFFFFu;
 }
 
-// Optimizers whose step divides by a root of the second moment.
-template <int OPT> struct HasRoot { static constexpr bool v = OPT == kAdam || OPT == kAdemamix; };
-// Index of the second moment (v, nu) in the state vector.
-template <int OPT> struct RootState { static constexpr int v = OPT == kAdemamix ? 2 : 1; };
+// Optimizers whose step divides by a root of a second-moment state.
+template <int OPT> struct HasRoot {
+    static constexpr bool v = OPT == kAdam || OPT == kAdemamix || OPT == kRmsprop || OPT == kAdagrad;
+};
+// Index of that state (v, nu, square_avg, sum) in the state vector.
+template <int OPT> struct RootState { static constexpr int v = OPT == kAdemamix ? 2 : (OPT == kAdam ? 1 : 0); };
 
-// Adam/AdEMAMix: the new states (Adam {m, v}; AdEMAMix {m1, m2, nu}).
+// Root optimizers: the new states (Adam {m, v}; AdEMAMix {m1, m2, nu}; RMSprop
+// {square_avg}; Adagrad {sum}).  RMSprop and Adagrad fold the decay into the
+// gradient, g' = g + wd * p.
 template <int OPT>
-__device__ __forceinline__ void moments(const StepScalars& s, float g, float st[3]) {
+__device__ __forceinline__ void moments(const StepScalars& s, float p, float g, float st[3]) {
     float t1, t2;
     if constexpr (OPT == kAdam) {
         t1 = s.b1 * st[0]; t2 = s.omb1 * g; st[0] = t1 + t2;
         const float gg = g * g;
         t1 = s.b2 * st[1]; t2 = s.omb2 * gg; st[1] = t1 + t2;
-    } else {
-        static_assert(OPT == kAdemamix, "moments of a root optimizer");
+    } else if constexpr (OPT == kAdemamix) {
         t1 = s.b1 * st[0]; t2 = s.omb1 * g; st[0] = t1 + t2;
         t1 = s.b3t * st[1]; t2 = s.omb3 * g; st[1] = t1 + t2;
         const float gg = g * g;
         t1 = s.b2 * st[2]; t2 = s.omb2 * gg; st[2] = t1 + t2;
+    } else if constexpr (OPT == kRmsprop) {
+        t1 = s.wd * p;
+        const float g2 = g + t1;
+        const float gg = g2 * g2;
+        t1 = s.b1 * st[0]; t2 = s.omb1 * gg; st[0] = t1 + t2;
+    } else {
+        static_assert(OPT == kAdagrad, "moments of a root optimizer");
+        t1 = s.wd * p;
+        const float g2 = g + t1;
+        const float gg = g2 * g2;
+        st[0] = st[0] + gg;
     }
 }
 
-// Adam/AdEMAMix: the parameter step from the new states, d = lr * u with
-// u = (m * ic1 [+ alpha_t * m2]) / (sqrt(v) * rs2 + eps).  UNSCALED: the caller has
-// checked that no second moment needs the scaled square root.
+// Root optimizers: the parameter step from the new states, d = lr * u with
+//   Adam/AdEMAMix  u = (m * ic1 [+ alpha_t * m2]) / (sqrt(v) * rs2 + eps)
+//   RMSprop/Adagrad  u = g' / (sqrt(state) + eps).
+// UNSCALED: the caller has checked that no state needs the scaled square root.
 template <int OPT, bool UNSCALED>
-__device__ __forceinline__ float root_delta(const StepScalars& s, const float st[3]) {
+__device__ __forceinline__ float root_delta(const StepScalars& s, float p, float g, const float st[3]) {
     const float v = st[RootState<OPT>::v];
     const float r = UNSCALED ? sqrt_rn_unscaled(v) : sqrtf(v);
-    float den = r * s.rs2;
-    den = den + s.eps;
-    float num = st[0] * s.ic1;
-    if constexpr (OPT == kAdemamix) {
-        const float t2 = s.alpha_t * st[1];
-        num = num + t2;
+    float u;
+    if constexpr (OPT == kAdam || OPT == kAdemamix) {
+        float den = r * s.rs2;
+        den = den + s.eps;
+        float num = st[0] * s.ic1;
+        if constexpr (OPT == kAdemamix) {
+            const float t2 = s.alpha_t * st[1];
+            num = num + t2;
+        }
+        u = num / den;
+    } else {
+        const float t1 = s.wd * p;
+        const float g2 = g + t1;
+        const float den = r + s.eps;
+        u = g2 / den;
     }
-    const float u = num / den;
     return s.lr * u;
 }
 
 // One element of one step.  st[] holds the decoded states on entry and the new
 // states on exit; the parameter step delta is returned through d.
-// Adam/AdEMAMix: st = {m, v} / {m1, m2, nu};  Momentum: {buf};  Lion: {m}.
+// Adam/AdEMAMix: st = {m, v} / {m1, m2, nu};  Momentum: {buf};  Lion: {m};
+// RMSprop: {square_avg};  Adagrad: {sum}.
 template <int OPT>
 __device__ __forceinline__ void update_elem(const StepScalars& s, float p, float g, float st[3], float& d) {
     float t1, t2;
     if constexpr (HasRoot<OPT>::v) {
-        moments<OPT>(s, g, st);
-        d = root_delta<OPT, false>(s, st);
+        moments<OPT>(s, p, g, st);
+        d = root_delta<OPT, false>(s, p, g, st);
     } else if constexpr (OPT == kMomentum) {
         float buf = st[0];
         t1 = s.wd * p;
@@ -438,7 +466,7 @@ __device__ __forceinline__ void update_elem(const StepScalars& s, float p, float
 
 template <int OPT>
 __device__ __forceinline__ float apply_step(const StepScalars& s, float p, float d) {
-    if constexpr (OPT == kMomentum) return p - d;
+    if constexpr (OPT == kMomentum || OPT == kRmsprop || OPT == kAdagrad) return p - d;   // decay in the gradient
     else { const float pd = p * s.decay; return pd - d; }
 }
 
@@ -750,7 +778,7 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
             float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
                            NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
             if constexpr (ROOT) {
-                moments<OPT>(a.s, gq[i], s3);
+                moments<OPT>(a.s, pf[q][i], gq[i], s3);
             } else {
                 float d;
                 update_elem<OPT>(a.s, pf[q][i], gq[i], s3, d);
@@ -770,7 +798,7 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
                 for (int i = 0; i < 4; ++i) {
                     const float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
                                          NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
-                    const float d = root_delta<OPT, decltype(unscaled)::value>(a.s, s3);
+                    const float d = root_delta<OPT, decltype(unscaled)::value>(a.s, pf[q][i], gq[i], s3);
                     dl[q][i] = live[q][i] ? d : 0.0f;
                 }
             };
@@ -1160,7 +1188,7 @@ __device__ __forceinline__ void step_one_tile_skip(const StepArgs& a, float* Q1,
     if (!__syncthreads_or(work)) return;
     const MapLDS M1{Q1, T1, B1}, M2{Q2, T2, B2};
     bool fast = true;
-    if constexpr (QUANT) fast = stage_maps<NMAPS>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote);
+    if constexpr (QUANT) fast = stage_maps<NMAPS, UnsignedState1<OPT>::v>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote);
     if (!work) return;
     if (full) {
         if (!QUANT || fast) {
@@ -1199,7 +1227,7 @@ __global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
         }
     }
     if constexpr (QUANT) {
-        if (stage_maps<NMAPS>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote))
+        if (stage_maps<NMAPS, UnsignedState1<OPT>::v>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote))
             step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, MULTI, true>(a, M1, M2, T0);
         else
             step_tiles<DT, OPT, BS, QUANT, SKIP, UNORM, MULTI, false>(a, M1, M2, T0);

@@ -13,6 +13,8 @@ hipError_t launch_step_adam(const StepArgs& a, int dtype, int bs, bool quant, bo
 hipError_t launch_step_ademamix(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s);
 hipError_t launch_step_momentum(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s);
 hipError_t launch_step_lion(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s);
+hipError_t launch_step_rmsprop(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s);
+hipError_t launch_step_adagrad(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s);
 
 hipError_t launch_quantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_dequantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);

@@ -165,6 +165,18 @@ def c4_embedding(optimizer: str = "momentum", skip_zeros: bool = True) -> Worklo
                     g_scale=1e-3, zero_row_frac=0.7)
 
 
+def f2_one_state_4096(optimizer: str, dtype: str = "f32") -> Workload:
+    """RMSprop / Adagrad 8-bit on the 4096x4096 shape: RMSprop with the optimizer
+    table's RMSprop8bit(p, 0.01, 0.9); Adagrad with lr 0.01, eps 1e-10."""
+    if optimizer == "rmsprop":
+        hp = dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8)
+    else:
+        hp = dict(optimizer="adagrad", lr=0.01, eps=1e-10)
+    hp.update(weight_decay=0.0, blocksize=256, skip_zeros=False, max_unorm=0.0)
+    return Workload(f"{optimizer}8bit_4096x4096_{dtype}_b256", 6, hp,
+                    [Tensor("w", (4096, 4096), dtype, True)], steps=20, p_scale=0.02, g_scale=1e-2)
+
+
 MIN_8BIT_SIZE = 4096
 
 

@@ -59,24 +59,34 @@ extern "C" {
 #define BITOPT_F16 1
 #define BITOPT_BF16 2
 
-/* Optimizers.  ADAM covers Adam and AdamW (decoupled decay when weight_decay > 0). */
+/* Optimizers.  ADAM covers Adam and AdamW (decoupled decay when weight_decay > 0).
+ * RMSPROP and ADAGRAD are the 1-state optimizers of the 8-bit PR's optimizer table
+ * (RMSprop8bit against torch.optim.RMSprop) and of the optimizer overview (Adagrad
+ * as its 1-state example), with the torch definitions. */
 #define BITOPT_ADAM 0
 #define BITOPT_ADEMAMIX 1
 #define BITOPT_MOMENTUM 2
 #define BITOPT_LION 3
+#define BITOPT_RMSPROP 4
+#define BITOPT_ADAGRAD 5
 
 /*
  * Hyper-parameters of one step ("optim_overview": Optimizer2State and
  * Optimizer1State argument lists).  Defaults there: lr 1e-3, betas (0.9, 0.999),
  * eps 1e-8, weight_decay 0, max_unorm 0 (off), skip_zeros false, alpha 0,
  * t_alpha / t_beta3 None (here: <= 0).
- *   optimizer     BITOPT_ADAM | BITOPT_ADEMAMIX | BITOPT_MOMENTUM | BITOPT_LION
+ *   optimizer     BITOPT_ADAM | BITOPT_ADEMAMIX | BITOPT_MOMENTUM | BITOPT_LION |
+ *                 BITOPT_RMSPROP | BITOPT_ADAGRAD
  *   beta1, beta2  Adam/AdEMAMix EMA rates; Momentum uses beta1 as the momentum;
- *                 Lion uses beta1 for the update interpolation, beta2 for its EMA.
+ *                 Lion uses beta1 for the update interpolation, beta2 for its EMA;
+ *                 RMSprop uses beta1 as the smoothing constant alpha of square_avg;
+ *                 Adagrad uses neither.
  *   beta3, alpha  AdEMAMix slow EMA rate and mixing weight.
  *   t_alpha, t_beta3  AdEMAMix warm-up lengths for alpha and beta3 (<= 0: none).
+ *   eps           added to the (bias-corrected, for Adam/AdEMAMix) root of the second
+ *                 moment: Adam, AdEMAMix, RMSprop, Adagrad.
  *   weight_decay  decoupled (p *= 1 - lr*wd) for Adam/AdEMAMix/Lion; added to the
- *                 gradient (g + wd*p) for Momentum.
+ *                 gradient (g + wd*p) for Momentum, RMSprop and Adagrad.
  *   max_unorm     > 0: per block, the update's L2 norm is capped at max_unorm times
  *                 the block's parameter L2 norm.
  *   skip_zeros    != 0: elements whose raw gradient is exactly +-0 keep their
@@ -168,8 +178,11 @@ BITOPT_API int bitopt_step_8bit_blockwise_2state(const bitopt_hparams* hp, int32
 
 /*
  * Fused 8-bit block-wise step of a 1-state optimizer (Optimizer1State): Momentum
- * (state1 = momentum_buffer) or Lion (state1 = exp_avg).  Arguments as above with
- * one state: state1 n bytes, absmax1 nb fp32, qmap1 the signed map.
+ * (state1 = momentum_buffer), Lion (state1 = exp_avg), RMSprop (state1 =
+ * square_avg) or Adagrad (state1 = sum of squared gradients).  Arguments as above
+ * with one state: state1 n bytes, absmax1 nb fp32, qmap1 the map of the state --
+ * the signed map for Momentum and Lion; RMSprop's and Adagrad's state is never
+ * negative, and the unsigned map spends all 256 codes on it.
  */
 BITOPT_API int bitopt_step_8bit_blockwise_1state(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
                                       int32_t dtype, int64_t n, uint8_t* state1, float* absmax1,

@@ -105,7 +105,7 @@ class Quant8:
         opt = hp["optimizer"]
         self.k1 = 2 if opt == "ademamix" else 1
         self.two = n_states(opt) >= 2
-        q1, q2 = oracle.dynamic_map(True), oracle.dynamic_map(False)
+        q1, q2 = oracle.dynamic_map(opt not in oracle.UNSIGNED_STATE1), oracle.dynamic_map(False)
         if maps is not None:
             q1 = maps[0] if maps[0] is not None else q1
             q2 = maps[1] if maps[1] is not None else q2
@@ -116,7 +116,8 @@ class Quant8:
         # device side (codebooks from the library's own builder)
         self.d = dict(p=to_dev(p0, dtype), s1=torch.zeros(self.k1 * n, dtype=torch.uint8, device="cuda"),
                       a1=torch.zeros(self.k1 * nb, dtype=torch.float32, device="cuda"),
-                      q1=bitopt.create_dynamic_map(True).cuda(), q2=bitopt.create_dynamic_map(False).cuda())
+                      q1=bitopt.create_dynamic_map(opt not in oracle.UNSIGNED_STATE1).cuda(),
+                      q2=bitopt.create_dynamic_map(False).cuda())
         if maps is not None:
             self.d["q1"] = torch.from_numpy(np.ascontiguousarray(q1, np.float32)).cuda()
             self.d["q2"] = torch.from_numpy(np.ascontiguousarray(q2, np.float32)).cuda()
@@ -170,7 +171,8 @@ class SampledTensor:
                       s2=torch.zeros(n, dtype=sd, device="cuda") if self.two else None,
                       a1=torch.zeros(self.k1 * nb, device="cuda") if eight else None,
                       a2=torch.zeros(nb, device="cuda") if (eight and self.two) else None)
-        self.q = (oracle.dynamic_map(True), oracle.dynamic_map(False))
+        self.unsigned1 = opt in oracle.UNSIGNED_STATE1
+        self.q = (oracle.dynamic_map(not self.unsigned1), oracle.dynamic_map(False))
         self.o = []
         for b in self.blocks:
             lo, hi = b * B, min(n, (b + 1) * B)
@@ -199,7 +201,8 @@ class SampledTensor:
             bitopt.step_8bit_blockwise_2state(self.hp, t, d["p"], g_dev, d["s1"], d["s2"], d["a1"], d["a2"],
                                               *self.qdev())
         elif self.eight:
-            bitopt.step_8bit_blockwise_1state(self.hp, t, d["p"], g_dev, d["s1"], d["a1"], self.qdev()[0])
+            bitopt.step_8bit_blockwise_1state(self.hp, t, d["p"], g_dev, d["s1"], d["a1"],
+                                              self.qdev()[1 if self.unsigned1 else 0])
         elif self.two:
             bitopt.step_32bit_2state(self.hp, t, d["p"], g_dev, d["s1"], d["s2"])
         else:

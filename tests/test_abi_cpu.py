@@ -60,6 +60,8 @@ HP_CASES = [
     dict(optimizer="ademamix", lr=1e-3, beta3=0.999, alpha=8.0),
     dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01),
     dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01),
+    dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8, weight_decay=0.01),
+    dict(optimizer="adagrad", lr=0.01, eps=1e-10, weight_decay=0.01),
 ]
 
 

@@ -13,6 +13,7 @@ checked in full.
      wd 0.01, skip_zeros on and off, 10 steps
   5. GPT-style 1.3B parameter set (146 8-bit bf16 tensors, 146 32-bit fp32 tensors
      below 4096 elements), one multi-tensor Adam step
+  and the 1-state RMSprop and Adagrad on the 4096x4096 shape (fp32, bf16), 20 steps.
 """
 import numpy as np
 import pytest
@@ -75,6 +76,12 @@ def test_config4_embedding_fp16(opt, skip):
     zr, nzr = np.nonzero(mask)[0][:8], np.nonzero(~mask)[0][:8]
     extra = np.concatenate([zr * 4, nzr * 4 + 1])          # 1024 columns = 4 blocks of 256 per row
     _run_single(wl, nsample=48, extra_blocks=extra)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("opt", ["rmsprop", "adagrad"])
+def test_one_state_rmsprop_adagrad_4096(opt, dtype):
+    _run_single(W.f2_one_state_4096(opt, dtype))
 
 
 def test_config5_gpt_1p3b_multi_tensor():

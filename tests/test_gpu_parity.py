@@ -3,8 +3,9 @@
 Every case starts both sides from the same seeded inputs; the oracle runs its own
 trajectory (it never takes data produced by the HIP path) and the two are
 compared after every step to the bar in tests/parity.py.  Sizes span several
-tiles and a ragged tail; both block sizes, all three parameter dtypes and all four
-optimizers are covered, with skip_zeros, max_unorm, the 32-bit mode, the codec,
+tiles and a ragged tail; both block sizes, all three parameter dtypes and all six
+optimizers (Adam, AdEMAMix, Momentum, Lion, RMSprop, Adagrad) are covered, with
+skip_zeros, max_unorm, custom and swapped maps, the 32-bit mode, the codec,
 unaligned buffers and empty inputs.
 """
 import numpy as np
@@ -24,6 +25,8 @@ OPTS = {
                      t_alpha=3, t_beta3=3, eps=1e-8, weight_decay=0.01),
     "momentum": dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01),
     "lion": dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01),
+    "rmsprop": dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8, weight_decay=0.01),
+    "adagrad": dict(optimizer="adagrad", lr=0.01, eps=1e-10, weight_decay=0.01),
 }
 
 
