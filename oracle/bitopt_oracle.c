@@ -380,9 +380,22 @@ static void step_block(const oref_hparams* h, const step_scalars* sc, int64_t b,
     const int64_t off = b * (int64_t)B;
     const int len = (int)((n - off) < B ? (n - off) : B);
 
-    float pv[OREF_MAXB], gv[OREF_MAXB], dv[OREF_MAXB];
-    float st[3][OREF_MAXB];
-    int skip[OREF_MAXB];
+    /* Blocks up to OREF_MAXB elements live on the stack; a tensor-wide block
+     * (blocksize 0: the whole tensor) on the heap. */
+    float pv_s[OREF_MAXB], gv_s[OREF_MAXB], dv_s[OREF_MAXB], st_s[3][OREF_MAXB];
+    int skip_s[OREF_MAXB];
+    float *pv = pv_s, *gv = gv_s, *dv = dv_s, *st[3] = {st_s[0], st_s[1], st_s[2]};
+    int* skip = skip_s;
+    float* heap = NULL;
+    int* heap_skip = NULL;
+    if (len > OREF_MAXB) {
+        heap = (float*)malloc(sizeof(float) * (size_t)len * 6);
+        heap_skip = (int*)malloc(sizeof(int) * (size_t)len);
+        if (!heap || !heap_skip) { free(heap); free(heap_skip); return; }
+        pv = heap; gv = heap + len; dv = heap + 2 * (size_t)len;
+        st[0] = heap + 3 * (size_t)len; st[1] = heap + 4 * (size_t)len; st[2] = heap + 5 * (size_t)len;
+        skip = heap_skip;
+    }
 
     void* arr[3]; int64_t eoff[3]; float* am[3]; int64_t aoff[3]; const float* q[3];
     for (int k = 0; k < ns; k++) slot_of(opt, k, n, nb, io, &arr[k], &eoff[k], &am[k], &aoff[k], &q[k]);
@@ -404,7 +417,7 @@ static void step_block(const oref_hparams* h, const step_scalars* sc, int64_t b,
         }
     }
     /* A block whose every gradient is zero is left completely untouched [P3]. */
-    if (h->skip_zeros && !any_live) return;
+    if (h->skip_zeros && !any_live) { free(heap); free(heap_skip); return; }
 
     /* Element updates: new states in st, parameter step in dv. */
     for (int i = 0; i < len; i++) {
@@ -526,13 +539,17 @@ static void step_block(const oref_hparams* h, const step_scalars* sc, int64_t b,
             for (int i = 0; i < len; i++) if (!skip[i]) dst[i] = st[k][i];
         }
     }
+    free(heap);
+    free(heap_skip);
 }
 
 static int check_hparams(const oref_hparams* h, int32_t step, int64_t n)
 {
     if (!h || step < 1 || n < 0) return -1;
     if (h->optimizer < OREF_ADAM || h->optimizer > OREF_ADAGRAD) return -1;
-    if (h->blocksize < 1 || h->blocksize > OREF_MAXB) return -1;
+    /* blocksize 0: one block spanning the tensor (non-block-wise 8-bit) */
+    if (h->blocksize < 0 || h->blocksize > OREF_MAXB) return -1;
+    if (h->blocksize == 0 && n > INT32_MAX) return -1;
     return 0;
 }
 
@@ -542,7 +559,8 @@ static int run_step(const oref_hparams* h, int32_t step, void* p, const void* g,
     if (check_hparams(h, step, n)) return -1;
     step_scalars sc;
     make_scalars(h, step, &sc);
-    const int B = h->blocksize;
+    if (n == 0) return 0;
+    const int B = h->blocksize ? h->blocksize : (int)n;
     const int64_t nb = (n + B - 1) / B;
     if (blocks) {
 #pragma omp parallel for schedule(static)

@@ -584,3 +584,64 @@ def test_block_subset_equals_full_step(oref):
         np.testing.assert_array_equal(sub_p[sl], full_p[sl])
         np.testing.assert_array_equal(sub_s["state1"][sl], full_s["state1"][sl])
         assert sub_s["absmax2"][b] == full_s["absmax2"][b]
+
+
+# ----------------------------------------------------------------------------- tensor-wide (non-block-wise) 8-bit
+
+def test_tensorwise_first_step_absmax_and_codes(oref):
+    """blocksize 0 = one block spanning the tensor.  From a zero state at t = 1 the new
+    states are m = (1-b1) g and v = (1-b2) g^2 (fp32 products), so the single absmax of
+    each state is that product at max |g|, and every code is the nearest entry of the
+    state normalised by it."""
+    n = 3 * 4096 + 123
+    g = W.normal_f32([81, 2], n, 0.01)
+    g[777] = 0.5                                         # one outlier sets the scale
+    hp = dict(optimizer="adam", lr=1e-3, blocksize=0)
+    p = W.normal_f32([81, 1], n, 0.02)
+    st = dict(state1=np.zeros(n, np.uint8), absmax1=np.zeros(1, f32), qmap1=oref.dynamic_map(True),
+              state2=np.zeros(n, np.uint8), absmax2=np.zeros(1, f32), qmap2=oref.dynamic_map(False))
+    _step8(oref, hp, 1, p, g, "f32", st)
+    sc = oref.step_scalars(hp, 1)
+    m = f32(sc["omb1"]) * g
+    v = f32(sc["omb2"]) * (g * g)
+    assert st["absmax1"][0] == np.abs(m).max() and st["absmax2"][0] == v.max()
+    for key, s, q, am in (("state1", m, st["qmap1"], st["absmax1"][0]), ("state2", v, st["qmap2"], st["absmax2"][0])):
+        x = s * (f32(1) / am)
+        np.testing.assert_array_equal(st[key], oref.nearest(q, x))
+
+
+def test_tensorwise_equals_one_block_of_the_same_size(oref):
+    n = 2048
+    p0, gs = _inputs(n, 4, 82)
+    outs = []
+    for B in (0, 2048):
+        hp = dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0, blocksize=B)
+        p = p0.copy()
+        st = _new8(oref, dict(hp, blocksize=2048), n)
+        for t, g in enumerate(gs, 1):
+            _step8(oref, hp, t, p, g, "f32", st)
+        outs.append((p, st))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    for k in outs[0][1]:
+        np.testing.assert_array_equal(outs[0][1][k], outs[1][1][k])
+
+
+def test_blockwise_is_more_precise_than_tensorwise(oref):
+    """The paper's motivation for block-wise quantization: an outlier in one place
+    coarsens a tensor-wide scale everywhere, while block-wise scales confine it to
+    its block."""
+    n = 64 * 256
+    g = W.normal_f32([83, 2], n, 0.01)
+    g[::4096] = 50.0                                     # four outliers
+    exact = f32(1 - 0.9) * g
+    errs = {}
+    for B in (256, 0):
+        hp = dict(optimizer="momentum", lr=0.0, beta1=0.9, blocksize=B)
+        st = _new8(oref, dict(hp, blocksize=256), n) if B else dict(
+            state1=np.zeros(n, np.uint8), absmax1=np.zeros(1, f32), qmap1=oref.dynamic_map(True))
+        p = np.zeros(n, f32)
+        _step8(oref, dict(optimizer="momentum", lr=0.0, beta1=0.9, blocksize=B), 1, p, g, "f32", st)
+        deq = oref.dequantize_blockwise(st["state1"], st["absmax1"], st["qmap1"], B if B else n)
+        small = np.abs(g) < 0.05
+        errs[B] = np.mean(np.abs(deq[small] - g[small]) / np.abs(g[small]))
+    assert errs[256] < 0.03 and errs[0] > 4 * errs[256], errs
