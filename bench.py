@@ -51,18 +51,34 @@ def workload_by_name(name):
         "rmsprop_bf16_b256": lambda: W.f2_one_state_4096("rmsprop", "bf16"),
         "adagrad_fp32_b256": lambda: W.f2_one_state_4096("adagrad", "f32"),
         "adagrad_bf16_b256": lambda: W.f2_one_state_4096("adagrad", "bf16"),
+        "adamw_fp32_tensorwise": lambda: W.f3_tensorwise_4096("f32"),
+        "adamw_bf16_tensorwise": lambda: W.f3_tensorwise_4096("bf16"),
         "adam_fp32_256x256": W.c1_adam_256,
         "gpt_1p3b": W.c5_gpt_1p3b,
     }
     return table[name]()
 
 
+NUM_STATES = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1, "rmsprop": 1, "adagrad": 1}
+
+
+def tensorwise_bytes_per_element(dtype: str, optimizer: str) -> float:
+    """The two-pass tensor-wide step: pass 1 reads g, the codes and (when the state
+    update uses it) p; pass 2 reads and writes like the block-wise step."""
+    ps = {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+    ns = NUM_STATES[optimizer]
+    needs_p = optimizer in ("momentum", "rmsprop", "adagrad")
+    return (3 * ps + 2 * ns) + (ps + ns + (ps if needs_p else 0))
+
+
 def workload_bytes(wl) -> float:
     """Algorithmic HBM bytes of one step over every tensor of the workload."""
-    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1, "rmsprop": 1, "adagrad": 1}[wl.hp["optimizer"]]
+    ns = NUM_STATES[wl.hp["optimizer"]]
     total = 0.0
     for t in wl.tensors:
-        if t.eightbit:
+        if t.eightbit and wl.hp["blocksize"] == 0:
+            total += tensorwise_bytes_per_element(t.dtype, wl.hp["optimizer"]) * t.numel
+        elif t.eightbit:
             total += W.bytes_per_element(t.dtype, ns, wl.hp["blocksize"]) * t.numel
         else:   # 32-bit states: read+write p, read g, read+write each fp32 state
             ps = {"f32": 4, "f16": 2, "bf16": 2}[t.dtype]
@@ -127,10 +143,12 @@ class Replica:
         self.n = n = t.numel
         hp = wl.hp
         B = hp["blocksize"]
-        nb = (n + B - 1) // B
+        self.tensorwise = B == 0
+        nb = 1 if self.tensorwise else (n + B - 1) // B
         dt = TORCH_DT[t.dtype]
         k1 = 2 if hp["optimizer"] == "ademamix" else 1
         self.two = hp["optimizer"] in ("adam", "adamw", "ademamix")
+        self.ws = torch.empty(bitopt.tensorwise_workspace_bytes(), dtype=torch.uint8, device=dev)
         p = W.normal_f32([wl.seed, 1, 0, r], n, wl.p_scale)
         g = W.normal_f32([wl.seed, 2, 0, r], n, wl.g_scale)
         if wl.zero_row_frac:
@@ -145,7 +163,10 @@ class Replica:
         self.a2 = torch.zeros(nb, dtype=torch.float32, device=dev) if self.two else None
 
     def step(self, hp, t, q1, q2):
-        if self.two:
+        if self.tensorwise:
+            bitopt.step_8bit_tensorwise(hp, t, self.p, self.g, self.s1, self.a1, q1, self.s2, self.a2,
+                                        q2 if self.two else None, workspace=self.ws)
+        elif self.two:
             bitopt.step_8bit_blockwise_2state(hp, t, self.p, self.g, self.s1, self.s2, self.a1, self.a2, q1, q2)
         else:
             bitopt.step_8bit_blockwise_1state(hp, t, self.p, self.g, self.s1, self.a1, q1)
@@ -159,7 +180,12 @@ class Replica:
         ptr = lambda x: ctypes.c_void_p(x.data_ptr())
         dt = bitopt.DTYPES[self.p.dtype]
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        if self.two:
+        if self.tensorwise:
+            f = L.bitopt_step_8bit_tensorwise
+            opt = lambda x: None if x is None else ptr(x)
+            tail = (ptr(self.s1), opt(self.s2), ptr(self.a1), opt(self.a2), ptr(q1),
+                    ptr(q2) if self.two else None, ptr(self.ws), stream)
+        elif self.two:
             f = L.bitopt_step_8bit_blockwise_2state
             tail = (ptr(self.s1), ptr(self.s2), ptr(self.a1), ptr(self.a2), ptr(q1), ptr(q2), stream)
         else:
@@ -193,7 +219,7 @@ def cpu_baseline(wl, target_s=15.0):
     def run(n, steps):
         p = W.to_dtype(W.normal_f32([wl.seed, 1, 0, 0], n_all, wl.p_scale, 0, n), t.dtype)
         g = W.to_dtype(W.normal_f32([wl.seed, 2, 0, 0], n_all, wl.g_scale, 0, n), t.dtype)
-        nb = (n + B - 1) // B
+        nb = 1 if B == 0 else (n + B - 1) // B
         s1, a1 = np.zeros(k1 * n, np.uint8), np.zeros(k1 * nb, np.float32)
         s2 = np.zeros(n, np.uint8) if two else None
         a2 = np.zeros(nb, np.float32) if two else None
@@ -202,13 +228,16 @@ def cpu_baseline(wl, target_s=15.0):
             oracle.step_8bit(hp, step, p, g, t.dtype, s1, a1, q1, s2, a2, q2 if two else None)
         return time.perf_counter() - t0
 
-    n0 = min(n_all, 256 * B)
-    dt0 = run(n0, 1)                                   # calibration
-    per_elem = dt0 / n0
-    if per_elem * n_all <= target_s:
-        n, steps = n_all, max(1, int(target_s / (per_elem * n_all)))
+    if B == 0:                                         # tensor-wide: one block, the whole tensor
+        n, steps = n_all, 1
     else:
-        n, steps = max(B, int(target_s / per_elem) // B * B), 1
+        n0 = min(n_all, 256 * B)
+        dt0 = run(n0, 1)                               # calibration
+        per_elem = dt0 / n0
+        if per_elem * n_all <= target_s:
+            n, steps = n_all, max(1, int(target_s / (per_elem * n_all)))
+        else:
+            n, steps = max(B, int(target_s / per_elem) // B * B), 1
     dt = run(n, steps)
     what = "the whole tensor" if n == n_all else f"the first {n} elements ({n // B} blocks of {B})"
     return {"value": n * steps / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
@@ -310,8 +339,7 @@ def profile(workload: str, outdir: str, steps: int):
     write_b = sum(ws) / len(ws) * w_scale * 1024.0
     wl = workload_by_name(workload)
     t = wl.tensors[0]
-    ns = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1, "rmsprop": 1, "adagrad": 1}[wl.hp["optimizer"]]
-    alg = W.bytes_per_element(t.dtype, ns, wl.hp["blocksize"]) * t.numel
+    alg = workload_bytes(wl)
     d = {"workload": workload, "kernel": kname, "source_hash": source_hash(),
          "kernel_trace_calls": calls, "kernel_trace_avg_us": avg_ns / 1e3,
          "fetch_kib_per_launch": sum(fs) / len(fs), "write_kib_per_launch": sum(ws) / len(ws),

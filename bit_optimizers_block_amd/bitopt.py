@@ -98,6 +98,8 @@ def lib():
             "bitopt_step_32bit_2state": ([HP, i32, P, P, i32, i64, P, P, P], ctypes.c_int),
             "bitopt_step_32bit_1state": ([HP, i32, P, P, i32, i64, P, P], ctypes.c_int),
             "bitopt_multi_workspace_bytes": ([i32], i64),
+            "bitopt_tensorwise_workspace_bytes": ([], i64),
+            "bitopt_step_8bit_tensorwise": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P, P], ctypes.c_int),
             "bitopt_step_multi": ([HP, i32, ctypes.POINTER(Tensor), i32, P, P, P, i64, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
@@ -232,6 +234,32 @@ def step_32bit_1state(hp, step, p, g, state1, stream=None):
     _need(p, "p"); _need(g, "g", p.dtype, n); _need(state1, "state1", torch.float32, n)
     _check(lib().bitopt_step_32bit_1state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
                                           _ptr(state1), _stream(stream)))
+
+
+def tensorwise_workspace_bytes() -> int:
+    return lib().bitopt_tensorwise_workspace_bytes()
+
+
+def step_8bit_tensorwise(hp, step, p, g, state1, absmax1, qmap1, state2=None, absmax2=None, qmap2=None,
+                         workspace=None, stream=None):
+    """Non-block-wise 8-bit step (hp blocksize 0): one absmax per state for the whole
+    tensor.  Returns the workspace tensor used (pass it back to reuse it)."""
+    h = make_hparams(hp)
+    n = p.numel()
+    k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
+    two = h.optimizer in (OPTIMIZERS["adam"], OPTIMIZERS["ademamix"])
+    _need(p, "p"); _need(g, "g", p.dtype, n)
+    _need(state1, "state1", torch.uint8, k * n); _need(absmax1, "absmax1", torch.float32, k)
+    _need(qmap1, "qmap1", torch.float32, 256)
+    if two:
+        _need(state2, "state2", torch.uint8, n); _need(absmax2, "absmax2", torch.float32, 1)
+        _need(qmap2, "qmap2", torch.float32, 256)
+    if workspace is None:
+        workspace = torch.empty(tensorwise_workspace_bytes(), dtype=torch.uint8, device=p.device)
+    _check(lib().bitopt_step_8bit_tensorwise(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
+                                             _ptr(state1), _ptr(state2), _ptr(absmax1), _ptr(absmax2),
+                                             _ptr(qmap1), _ptr(qmap2), _ptr(workspace), _stream(stream)))
+    return workspace
 
 
 def multi_workspace_bytes(count: int) -> int:

@@ -31,7 +31,7 @@ FLAGS = [
 ]
 
 SOURCES = ["bitopt_api.cpp", "codec.hip", "step_adam.hip", "step_ademamix.hip",
-           "step_momentum.hip", "step_lion.hip", "step_rmsprop.hip", "step_adagrad.hip"]
+           "step_momentum.hip", "step_lion.hip", "step_rmsprop.hip", "step_adagrad.hip", "tensorwise.hip"]
 
 
 def _compile(src: str, extra=()) -> str:

@@ -278,6 +278,40 @@ int bitopt_step_32bit_1state(const bitopt_hparams* hp, int32_t step, void* p, co
     return run_step(hp, step, p, g, dtype, n, state1, nullptr, nullptr, nullptr, nullptr, nullptr, false, stream, fn);
 }
 
+int64_t bitopt_tensorwise_workspace_bytes(void) { return (int64_t)bitopt::tensorwise_workspace_words() * 4; }
+
+int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype,
+                                int64_t n, uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
+                                const float* qmap1, const float* qmap2, void* workspace, void* stream) {
+    const char* fn = "bitopt_step_8bit_tensorwise";
+    if (!hp) return fail(BITOPT_ERR_INVALID_ARG, "%s: hp is NULL", fn);
+    if (hp->blocksize != 0)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: blocksize must be 0 (one block for the tensor), got %d", fn,
+                    hp->blocksize);
+    bitopt_hparams h = *hp;
+    h.blocksize = 256;                         // the shared checks know block sizes only
+    if (int rc = check_hparams(&h, step, n, fn)) return rc;
+    if (hp->max_unorm > 0.0f)
+        return fail(BITOPT_ERR_UNSUPPORTED, "%s: max_unorm is not supported by the tensor-wide step", fn);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
+    if (n == 0) return ok();
+    if (!p || !g || !state1 || !absmax1 || !qmap1 || !workspace || (two && (!state2 || !absmax2 || !qmap2)))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(workspace, 4)) return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace not 4-byte aligned", fn);
+    bitopt::StepArgs a{};
+    a.p = p; a.g = g; a.s1 = state1; a.s2 = two ? state2 : nullptr; a.a1 = absmax1; a.a2 = two ? absmax2 : nullptr;
+    a.q1 = qmap1; a.q2 = two ? qmap2 : qmap1;
+    a.n = n;
+    a.nb = 1;
+    a.s = make_scalars(h, step);
+    a.vec = vec_ok(&h, p, g, dtype, n, state1, two ? state2 : nullptr) ? 1 : 0;
+    a.ws = static_cast<uint32_t*>(workspace);
+    hipError_t e = bitopt::launch_tensorwise(a, hp->optimizer, dtype, hp->skip_zeros != 0,
+                                             reinterpret_cast<hipStream_t>(stream));
+    return device_status(e, fn);
+}
+
 int64_t bitopt_multi_workspace_bytes(int32_t count) {
     if (count < 0) return -1;
     return (int64_t)count * (int64_t)sizeof(bitopt::TensorDesc);

@@ -77,6 +77,8 @@ struct StepArgs {
     const TensorDesc* table;   // multi-tensor launch: ntab tensors (the fields above unused)
     int32_t ntab;
     int64_t total_tiles;
+    uint32_t* ws;              // tensor-wide step: workspace shared by its passes
+    int32_t parts;             // tensor-wide step: groups of pass 1 (partial results in ws)
 };
 
 template <int OPT> struct NumStates { static constexpr int v = OPT == kAdemamix ? 3 : (OPT == kAdam ? 2 : 1); };

@@ -16,6 +16,10 @@ hipError_t launch_step_lion(const StepArgs& a, int dtype, int bs, bool quant, bo
 hipError_t launch_step_rmsprop(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s);
 hipError_t launch_step_adagrad(const StepArgs& a, int dtype, int bs, bool quant, bool skip, bool unorm, hipStream_t s);
 
+// Tensor-wide (non-block-wise) 8-bit step: clear, pass 1 (absmax), pass 2 (apply).
+hipError_t launch_tensorwise(const StepArgs& a, int opt, int dtype, bool skip, hipStream_t s);
+int tensorwise_workspace_words();
+
 hipError_t launch_quantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_dequantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 

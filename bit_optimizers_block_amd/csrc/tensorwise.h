@@ -1,0 +1,238 @@
+// tensorwise.h -- the non-block-wise (tensor-wide) 8-bit step: every state has one
+// absmax for the whole tensor.  The new absmax depends on every element's new state,
+// so the step takes three launches:
+//   pass 1   reads g, the codes and (where the state update uses it) p, computes the
+//            new states, and each group writes its max |state| per state (and whether
+//            it saw a nonzero gradient) to its own workspace slot -- no atomics, so
+//            no contention on a few addresses and a deterministic result;
+//   reduce   one group folds the slots into the tensor-wide absmax and copies the
+//            old absmax next to it (pass 2 decodes with the copy, so it may
+//            overwrite the absmax array);
+//   pass 2   reads everything again, recomputes the same values, writes p, encodes
+//            the states with the tensor-wide scale and writes the codes and absmax.
+// Workspace words: [0, 3) new absmax bits per state, [3, 6) old absmax, [6] nonzero
+// gradient seen; then kTwWordsPerPart words per group of pass 1 (a maximum of
+// non-negative floats is taken on their bit patterns as integers).
+// The element arithmetic is update_elem / apply_step / encode of kernels.h, so the
+// results equal one block spanning the tensor.
+#pragma once
+
+#include "kernels.h"
+
+namespace bitopt {
+
+constexpr int kTwHead = 8;                 // words before the per-group slots
+constexpr int kTwWordsPerPart = 4;         // max bits of up to three states, nonzero-gradient flag
+constexpr int kTwMaxParts = 1024;          // groups of pass 1 (grid-stride beyond)
+constexpr int kTwWords = kTwHead + kTwWordsPerPart * kTwMaxParts;
+
+// State updates that read the parameter (weight decay folded into the gradient).
+template <int OPT> struct StateNeedsP {
+    static constexpr bool v = OPT == kMomentum || OPT == kRmsprop || OPT == kAdagrad;
+};
+
+// One quad of lane l of a tile: element indices e .. e+3 (FULL: in range and aligned).
+template <int DT, int OPT, bool SKIP, bool FULL, bool NEEDP>
+__device__ __forceinline__ void tw_quad(const StepArgs& a, const float* const (&Q)[2], const float (&A)[3],
+                                        int64_t e, float (&pv)[4], float (&st)[3][4], float (&dl)[4],
+                                        uint32_t& livem) {
+    constexpr int NS = NumStates<OPT>::v;
+    const int64_t n = a.n;
+    float gv[4];
+    if constexpr (FULL) {
+        if constexpr (NEEDP) load4<DT>(a.p, e, pv);
+        else pv[0] = pv[1] = pv[2] = pv[3] = 0.0f;
+        load4<DT>(a.g, e, gv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool valid = e + i < n;
+            pv[i] = (NEEDP && valid) ? load1<DT>(a.p, e + i) : 0.0f;
+            gv[i] = valid ? load1<DT>(a.g, e + i) : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int slot = Slot<OPT>::which(k);
+        const uint8_t* cp = reinterpret_cast<const uint8_t*>(slot ? a.s2 : a.s1) + Slot<OPT>::elem_off(k, n);
+        if constexpr (FULL) {
+            const uint32_t w = ld_stream(reinterpret_cast<const uint32_t*>(cp + e));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[k][i] = Q[slot][(w >> (8 * i)) & 0xffu] * A[k];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[k][i] = e + i < n ? Q[slot][gbl(cp)[e + i]] * A[k] : 0.0f;
+        }
+    }
+    livem = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool valid = FULL || e + i < n;
+        const bool live = valid && !(SKIP && gv[i] == 0.0f);
+        livem |= live ? 1u << i : 0u;
+        float s3[3] = {st[0][i], NS > 1 ? st[NS > 1 ? 1 : 0][i] : 0.0f, NS > 2 ? st[NS > 2 ? 2 : 0][i] : 0.0f};
+        float d;
+        update_elem<OPT>(a.s, pv[i], gv[i], s3, d);
+        dl[i] = live ? d : 0.0f;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) st[k][i] = live ? s3[k] : st[k][i];
+    }
+}
+
+template <int OPT>
+__device__ __forceinline__ void tw_old_absmax(const StepArgs& a, float (&A)[3]) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) A[k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NumStates<OPT>::v; ++k) {
+        const float* am = (Slot<OPT>::which(k) ? a.a2 : a.a1) + Slot<OPT>::block_off(k, 1);
+        A[k] = gbl(am)[0];
+    }
+}
+
+// Pass 1: the tensor-wide max |new state| of each state.
+template <int DT, int OPT, bool SKIP>
+__global__ __launch_bounds__(kThreads) void k_tw_max(StepArgs a) {
+    constexpr int NS = NumStates<OPT>::v;
+    constexpr bool NEEDP = StateNeedsP<OPT>::v;
+    constexpr int NMAPS = (OPT == kAdam || OPT == kAdemamix) ? 2 : 1;
+    __shared__ float Q1[256], Q2[256];
+    Q1[threadIdx.x] = gbl(a.q1)[threadIdx.x];
+    if constexpr (NMAPS > 1) Q2[threadIdx.x] = gbl(a.q2)[threadIdx.x];
+    __syncthreads();
+    const float* const Q[2] = {Q1, Q2};
+    float A[3];
+    tw_old_absmax<OPT>(a, A);
+
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerGroup;
+    const int64_t ntiles = (a.n + 1023) / 1024;
+    float mx[3] = {0.0f, 0.0f, 0.0f};
+    uint32_t anyl = 0;
+    for (int64_t t = wave_id(); t < ntiles; t += stride) {
+        const bool full = a.vec && (t + 1) * 1024 <= a.n;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = t * 1024 + q * 256 + lane * 4;
+            float pv[4], st[3][4], dl[4];
+            uint32_t livem;
+            if (full) tw_quad<DT, OPT, SKIP, true, NEEDP>(a, Q, A, e, pv, st, dl, livem);
+            else tw_quad<DT, OPT, SKIP, false, NEEDP>(a, Q, A, e, pv, st, dl, livem);
+            anyl |= livem;
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx[k] = fmaxf(mx[k], fabsf(st[k][i]));
+        }
+    }
+    // this group's slot: per-wave results through LDS, one lane writes
+    __shared__ uint32_t part[kWavesPerGroup][kTwWordsPerPart];
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const float m = k < NS ? wave_max_nonneg(mx[k]) : 0.0f;
+        if (lane == 0) part[wave][k] = __float_as_uint(m);
+    }
+    const bool any = wave_any(anyl != 0u);
+    if (lane == 0) part[wave][3] = any ? 1u : 0u;
+    __syncthreads();
+    if (threadIdx.x < kTwWordsPerPart) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) v = max(v, part[w][threadIdx.x]);
+        a.ws[kTwHead + kTwWordsPerPart * blockIdx.x + threadIdx.x] = v;
+    }
+}
+
+// Fold the pass-1 slots into the tensor-wide results; copy the old absmax.
+template <int OPT>
+__global__ __launch_bounds__(kThreads) void k_tw_reduce(StepArgs a) {
+    constexpr int NS = NumStates<OPT>::v;
+    __shared__ uint32_t red[kWavesPerGroup][kTwWordsPerPart];
+    uint32_t v[kTwWordsPerPart] = {0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < a.parts; i += kThreads)
+#pragma unroll
+        for (int j = 0; j < kTwWordsPerPart; ++j) v[j] = max(v[j], a.ws[kTwHead + kTwWordsPerPart * i + j]);
+#pragma unroll
+    for (int j = 0; j < kTwWordsPerPart; ++j) {
+        const uint32_t w = __float_as_uint(wave_max_nonneg(__uint_as_float(v[j])));
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][j] = w;
+    }
+    __syncthreads();
+    if (threadIdx.x < kTwWordsPerPart) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) r = max(r, red[w][threadIdx.x]);
+        a.ws[threadIdx.x < 3 ? threadIdx.x : 6] = r;
+    }
+    if (threadIdx.x < NS) {
+        float A[3];
+        tw_old_absmax<OPT>(a, A);
+        a.ws[3 + threadIdx.x] = __float_as_uint(A[threadIdx.x]);
+    }
+}
+
+// Pass 2: recompute, write p, encode with the tensor-wide scale, write codes and absmax.
+template <int DT, int OPT, bool SKIP>
+__global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
+    constexpr int NS = NumStates<OPT>::v;
+    constexpr int NMAPS = (OPT == kAdam || OPT == kAdemamix) ? 2 : 1;
+    if (SKIP && a.ws[6] == 0u) return;                 // no nonzero gradient: nothing is written
+    __shared__ float Q1[256], Q2[256], T1[256], T2[256];
+    __shared__ __attribute__((aligned(16))) uint8_t B1[search::kNB];
+    __shared__ __attribute__((aligned(16))) uint8_t B2[search::kNB];
+    __shared__ uint32_t vote[kWavesPerGroup];
+    const bool fast = stage_maps<NMAPS, UnsignedState1<OPT>::v>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote);
+    const MapLDS M[2] = {MapLDS{Q1, T1, B1}, MapLDS{Q2, T2, B2}};
+    const float* const Q[2] = {Q1, Q2};
+    float A[3], r[3], c[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        A[k] = k < NS ? __uint_as_float(a.ws[3 + k]) : 0.0f;
+        const float An = k < NS ? __uint_as_float(a.ws[k]) : 0.0f;
+        block_recip(An, r[k], c[k]);
+    }
+    const int lane = threadIdx.x & 63;
+    if (blockIdx.x == 0 && threadIdx.x < NS) {
+        const int k = threadIdx.x;
+        float* am = (Slot<OPT>::which(k) ? a.a2 : a.a1) + Slot<OPT>::block_off(k, 1);
+        gbl(am)[0] = __uint_as_float(a.ws[k]);
+    }
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerGroup;
+    const int64_t ntiles = (a.n + 1023) / 1024;
+    for (int64_t t = wave_id(); t < ntiles; t += stride) {
+        const bool full = a.vec && (t + 1) * 1024 <= a.n;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = t * 1024 + q * 256 + lane * 4;
+            float pv[4], st[3][4], dl[4];
+            uint32_t livem;
+            if (full) tw_quad<DT, OPT, SKIP, true, true>(a, Q, A, e, pv, st, dl, livem);
+            else tw_quad<DT, OPT, SKIP, false, true>(a, Q, A, e, pv, st, dl, livem);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[i] = ((livem >> i) & 1u) ? apply_step<OPT>(a.s, pv[i], dl[i]) : pv[i];
+            if (full) {
+                store4<DT>(a.p, e, pv);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (e + i < a.n) store1<DT>(a.p, e + i, pv[i]);
+            }
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                const int slot = Slot<OPT>::which(k);
+                uint32_t w = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float y = (st[k][i] * c[k]) * r[k];
+                    w |= (fast ? encode<true>(M[slot], y) : encode<false>(M[slot], y)) << (8 * i);
+                }
+                uint8_t* cp = reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + Slot<OPT>::elem_off(k, a.n);
+                if (full) store_code_word<true>(cp, e, a.n, w);
+                else store_code_word<false>(cp, e, a.n, w);
+            }
+        }
+    }
+}
+
+}  // namespace bitopt

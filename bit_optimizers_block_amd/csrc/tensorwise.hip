@@ -1,0 +1,53 @@
+// Kernel instantiations and launches of the tensor-wide (non-block-wise) 8-bit step.
+#include "launch.h"
+#include "tensorwise.h"
+
+namespace bitopt {
+namespace {
+
+template <int DT, int OPT, bool SKIP>
+hipError_t tw_launch(const StepArgs& a0, hipStream_t s) {
+    StepArgs a = a0;
+    const dim3 grid = tile_grid(a.n, 1024);
+    const int64_t tiles = (a.n + 1023) / 1024;
+    int64_t parts = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+    if (parts > kTwMaxParts) parts = kTwMaxParts;
+    a.parts = (int32_t)parts;
+    hipLaunchKernelGGL((k_tw_max<DT, OPT, SKIP>), dim3((unsigned)parts), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_tw_reduce<OPT>), dim3(1), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_tw_apply<DT, OPT, SKIP>), grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DT, int OPT>
+hipError_t tw_skip(const StepArgs& a, bool skip, hipStream_t s) {
+    return skip ? tw_launch<DT, OPT, true>(a, s) : tw_launch<DT, OPT, false>(a, s);
+}
+
+template <int OPT>
+hipError_t tw_dtype(const StepArgs& a, int dtype, bool skip, hipStream_t s) {
+    switch (dtype) {
+    case kF32: return tw_skip<kF32, OPT>(a, skip, s);
+    case kF16: return tw_skip<kF16, OPT>(a, skip, s);
+    case kBF16: return tw_skip<kBF16, OPT>(a, skip, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int tensorwise_workspace_words() { return kTwWords; }
+
+hipError_t launch_tensorwise(const StepArgs& a, int opt, int dtype, bool skip, hipStream_t s) {
+    switch (opt) {
+    case kAdam: return tw_dtype<kAdam>(a, dtype, skip, s);
+    case kAdemamix: return tw_dtype<kAdemamix>(a, dtype, skip, s);
+    case kMomentum: return tw_dtype<kMomentum>(a, dtype, skip, s);
+    case kLion: return tw_dtype<kLion>(a, dtype, skip, s);
+    case kRmsprop: return tw_dtype<kRmsprop>(a, dtype, skip, s);
+    case kAdagrad: return tw_dtype<kAdagrad>(a, dtype, skip, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace bitopt

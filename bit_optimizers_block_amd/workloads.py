@@ -177,6 +177,14 @@ def f2_one_state_4096(optimizer: str, dtype: str = "f32") -> Workload:
                     [Tensor("w", (4096, 4096), dtype, True)], steps=20, p_scale=0.02, g_scale=1e-2)
 
 
+def f3_tensorwise_4096(dtype: str = "f32") -> Workload:
+    """AdamW 8-bit on the 4096x4096 shape with one absmax per state for the whole
+    tensor (blocksize 0): the non-block-wise form, same hyper-parameters as the
+    block-wise AdamW workload."""
+    return Workload(f"adamw8bit_4096x4096_{dtype}_tensorwise", 2, _adam_hp(blocksize=0, weight_decay=0.01),
+                    [Tensor("w", (4096, 4096), dtype, True)], steps=20, p_scale=0.02, g_scale=1e-2)
+
+
 MIN_8BIT_SIZE = 4096
 
 

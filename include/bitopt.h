@@ -225,6 +225,31 @@ typedef struct bitopt_tensor {
     int32_t is_8bit;
 } bitopt_tensor;
 
+/*
+ * Non-block-wise ("tensor-wide") 8-bit step: each state keeps ONE absmax for the
+ * whole tensor instead of one per block -- the form that block-wise quantization
+ * ("8-bit Optimizers via Block-wise Quantization", abstract) improves on, kept here
+ * to measure that claim.  The same update, codes and maps as the block-wise steps:
+ *   absmax1  device fp32, 1 entry (AdEMAMix: 2, m1's then m2's)
+ *   state2, absmax2 (1 entry), qmap2  2-state optimizers; NULL for 1-state ones
+ *   hp->blocksize must be 0 (one block spanning the tensor); hp->max_unorm > 0 gives
+ *            BITOPT_ERR_UNSUPPORTED (no per-tensor norm pass)
+ *   workspace device memory of at least bitopt_tensorwise_workspace_bytes() bytes,
+ *            4-byte aligned, caller-owned and overwritten; calls that may run
+ *            concurrently must not share one
+ * The new absmax depends on every element, so the step is three launches on
+ * `stream`: a pass that reads g, the codes and (Momentum, RMSprop, Adagrad) p and
+ * leaves each group's max |new state| in the workspace; a one-group reduction of
+ * those; a pass that reads everything again, writes p, encodes with the
+ * tensor-wide scale and writes codes and absmax.  The results equal the
+ * block-wise step with one block of n elements (deterministic: no atomics).
+ */
+BITOPT_API int64_t bitopt_tensorwise_workspace_bytes(void);
+BITOPT_API int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                           int32_t dtype, int64_t n, uint8_t* state1, uint8_t* state2,
+                                           float* absmax1, float* absmax2, const float* qmap1,
+                                           const float* qmap2, void* workspace, void* stream);
+
 /* Bytes of device workspace bitopt_step_multi needs for `count` tensors (< 0 if count < 0). */
 BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
 

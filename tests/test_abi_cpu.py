@@ -155,3 +155,26 @@ def test_multi_argument_errors(B):
     arr[0] = B.Tensor(16, 16, 16, 16, 16, 16, 0, 0, 1)                                      # n == 0 entries skipped
     arr[1] = B.Tensor(None, None, None, None, None, None, 0, 0, 1)
     assert L.bitopt_step_multi(ctypes.byref(h), 1, arr, 2, None, None, P, 1000, None) == B.OK
+
+
+def test_tensorwise_argument_errors(B):
+    L = B.lib()
+    E = B.ERR_INVALID_ARG
+    P = ctypes.c_void_p(16)
+    assert L.bitopt_tensorwise_workspace_bytes() >= 28
+    h = B.make_hparams(dict(optimizer="adam", blocksize=0))
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 1, P, P, 0, 0, P, P, P, P, P, P, P, None) == B.OK
+    hb = B.make_hparams(dict(optimizer="adam", blocksize=256))
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(hb), 1, P, P, 0, 16, P, P, P, P, P, P, P, None) == E
+    assert "blocksize" in B.last_error()
+    hu = B.make_hparams(dict(optimizer="adam", blocksize=0, max_unorm=1.0))
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(hu), 1, P, P, 0, 16, P, P, P, P, P, P, P, None) == \
+        B.ERR_UNSUPPORTED
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 1, P, P, 0, 16, P, P, P, P, P, P, None, None) == E
+    assert "NULL" in B.last_error()
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 1, P, P, 0, 16, P, None, P, P, P, P, P, None) == E
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 1, P, P, 0, 16, P, P, P, P, P, P,
+                                         ctypes.c_void_p(18), None) == E                      # misaligned
+    h1 = B.make_hparams(dict(optimizer="rmsprop", blocksize=0))                               # 1-state: no state2
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h1), 1, P, P, 0, 0, P, None, P, None, P, None, P, None) == B.OK
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 0, P, P, 0, 16, P, P, P, P, P, P, P, None) == E
