@@ -53,6 +53,7 @@ def workload_by_name(name):
         "adagrad_bf16_b256": lambda: W.f2_one_state_4096("adagrad", "bf16"),
         "adamw_fp32_tensorwise": lambda: W.f3_tensorwise_4096("f32"),
         "adamw_bf16_tensorwise": lambda: W.f3_tensorwise_4096("bf16"),
+        "adamw_fp32_b256_paged": lambda: W.f4_paged_4096("f32"),
         "adam_fp32_256x256": W.c1_adam_256,
         "gpt_1p3b": W.c5_gpt_1p3b,
     }
@@ -157,10 +158,19 @@ class Replica:
             g.reshape(rows, -1)[mask] = 0.0
         self.p = torch.from_numpy(p).to(dev).to(dt)
         self.g = torch.from_numpy(g).to(dev).to(dt)
-        self.s1 = torch.zeros(k1 * n, dtype=torch.uint8, device=dev)
-        self.a1 = torch.zeros(k1 * nb, dtype=torch.float32, device=dev)
-        self.s2 = torch.zeros(n, dtype=torch.uint8, device=dev) if self.two else None
-        self.a2 = torch.zeros(nb, dtype=torch.float32, device=dev) if self.two else None
+        if wl.extra.get("paged"):
+            # optimizer state in pinned host memory mapped into the GPU address space
+            def z(numel, dt):
+                t_ = bitopt.host_state(numel, dt)
+                t_.zero_()
+                return t_
+        else:
+            def z(numel, dt):
+                return torch.zeros(numel, dtype=dt, device=dev)
+        self.s1 = z(k1 * n, torch.uint8)
+        self.a1 = z(k1 * nb, torch.float32)
+        self.s2 = z(n, torch.uint8) if self.two else None
+        self.a2 = z(nb, torch.float32) if self.two else None
 
     def step(self, hp, t, q1, q2):
         if self.tensorwise:
@@ -475,6 +485,8 @@ def main():
         cfg = {"workload": wl.name, "optimizer": hp["optimizer"], "shape": list(t.shape),
                "param_dtype": t.dtype, "blocksize": B, "weight_decay": hp.get("weight_decay", 0.0),
                "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps)}
+        if wl.extra.get("paged"):
+            cfg["state_memory"] = "pinned host (paged)"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gelem/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(avg_ms, 5),

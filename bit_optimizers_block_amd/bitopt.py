@@ -99,6 +99,8 @@ def lib():
             "bitopt_step_32bit_1state": ([HP, i32, P, P, i32, i64, P, P], ctypes.c_int),
             "bitopt_multi_workspace_bytes": ([i32], i64),
             "bitopt_tensorwise_workspace_bytes": ([], i64),
+            "bitopt_host_state_alloc": ([i64, ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
+            "bitopt_host_state_free": ([P], ctypes.c_int),
             "bitopt_step_8bit_tensorwise": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P, P], ctypes.c_int),
             "bitopt_step_multi": ([HP, i32, ctypes.POINTER(Tensor), i32, P, P, P, i64, P], ctypes.c_int),
         }
@@ -128,12 +130,47 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# --------------------------------------------------------------- state outside HBM
+
+_host_states = {}     # address -> bytes of live bitopt_host_state_alloc buffers
+
+
+def _free_host_state(ptr):
+    _host_states.pop(ptr, None)
+    lib().bitopt_host_state_free(ctypes.c_void_p(ptr))
+
+
+def host_state(numel: int, dtype=torch.uint8) -> torch.Tensor:
+    """A CPU tensor over pinned host memory mapped into the GPU address space
+    (bitopt_host_state_alloc): optimizer state kept outside HBM, which every step
+    accepts in place of device state.  The memory is freed when the tensor is
+    garbage-collected; synchronize the streams that use it before dropping it."""
+    import weakref
+    import numpy as np
+    nbytes = int(numel) * torch.empty(0, dtype=dtype).element_size()
+    ptr = ctypes.c_void_p()
+    _check(lib().bitopt_host_state_alloc(max(nbytes, 1), ctypes.byref(ptr)))
+    buf = (ctypes.c_uint8 * max(nbytes, 1)).from_address(ptr.value)
+    arr = np.frombuffer(buf, dtype=np.uint8)[:nbytes]
+    _host_states[ptr.value] = max(nbytes, 1)
+    weakref.finalize(buf, _free_host_state, ptr.value)
+    return torch.from_numpy(arr).view(dtype)
+
+
+def _is_host_state(t) -> bool:
+    a = t.data_ptr()
+    return any(p <= a and a + t.numel() * t.element_size() <= p + n for p, n in _host_states.items())
+
+
 def _need(t, name, dtype=None, numel=None, device=True):
     if t is None:
         raise ValueError(f"{name} is required")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if device and not t.is_cuda:
+    if device == "state":
+        if not (t.is_cuda or _is_host_state(t)):
+            raise ValueError(f"{name} must be a device tensor or a host_state() tensor")
+    elif device and not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
@@ -200,8 +237,8 @@ def step_8bit_blockwise_2state(hp, step, p, g, state1, state2, absmax1, absmax2,
     k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
     nb = nblocks(n, h.blocksize)
     _need(p, "p"); _need(g, "g", p.dtype, n)
-    _need(state1, "state1", torch.uint8, k * n); _need(state2, "state2", torch.uint8, n)
-    _need(absmax1, "absmax1", torch.float32, k * nb); _need(absmax2, "absmax2", torch.float32, nb)
+    _need(state1, "state1", torch.uint8, k * n, device="state"); _need(state2, "state2", torch.uint8, n, device="state")
+    _need(absmax1, "absmax1", torch.float32, k * nb, device="state"); _need(absmax2, "absmax2", torch.float32, nb, device="state")
     _need(qmap1, "qmap1", torch.float32, 256); _need(qmap2, "qmap2", torch.float32, 256)
     _check(lib().bitopt_step_8bit_blockwise_2state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
                                                    _ptr(state1), _ptr(state2), _ptr(absmax1), _ptr(absmax2),
@@ -212,7 +249,7 @@ def step_8bit_blockwise_1state(hp, step, p, g, state1, absmax1, qmap1, stream=No
     h = make_hparams(hp)
     n = p.numel()
     _need(p, "p"); _need(g, "g", p.dtype, n)
-    _need(state1, "state1", torch.uint8, n); _need(absmax1, "absmax1", torch.float32, nblocks(n, h.blocksize))
+    _need(state1, "state1", torch.uint8, n, device="state"); _need(absmax1, "absmax1", torch.float32, nblocks(n, h.blocksize), device="state")
     _need(qmap1, "qmap1", torch.float32, 256)
     _check(lib().bitopt_step_8bit_blockwise_1state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
                                                    _ptr(state1), _ptr(absmax1), _ptr(qmap1), _stream(stream)))
@@ -223,7 +260,7 @@ def step_32bit_2state(hp, step, p, g, state1, state2, stream=None):
     n = p.numel()
     k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
     _need(p, "p"); _need(g, "g", p.dtype, n)
-    _need(state1, "state1", torch.float32, k * n); _need(state2, "state2", torch.float32, n)
+    _need(state1, "state1", torch.float32, k * n, device="state"); _need(state2, "state2", torch.float32, n, device="state")
     _check(lib().bitopt_step_32bit_2state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
                                           _ptr(state1), _ptr(state2), _stream(stream)))
 
@@ -231,7 +268,7 @@ def step_32bit_2state(hp, step, p, g, state1, state2, stream=None):
 def step_32bit_1state(hp, step, p, g, state1, stream=None):
     h = make_hparams(hp)
     n = p.numel()
-    _need(p, "p"); _need(g, "g", p.dtype, n); _need(state1, "state1", torch.float32, n)
+    _need(p, "p"); _need(g, "g", p.dtype, n); _need(state1, "state1", torch.float32, n, device="state")
     _check(lib().bitopt_step_32bit_1state(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
                                           _ptr(state1), _stream(stream)))
 
@@ -249,10 +286,10 @@ def step_8bit_tensorwise(hp, step, p, g, state1, absmax1, qmap1, state2=None, ab
     k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
     two = h.optimizer in (OPTIMIZERS["adam"], OPTIMIZERS["ademamix"])
     _need(p, "p"); _need(g, "g", p.dtype, n)
-    _need(state1, "state1", torch.uint8, k * n); _need(absmax1, "absmax1", torch.float32, k)
+    _need(state1, "state1", torch.uint8, k * n, device="state"); _need(absmax1, "absmax1", torch.float32, k, device="state")
     _need(qmap1, "qmap1", torch.float32, 256)
     if two:
-        _need(state2, "state2", torch.uint8, n); _need(absmax2, "absmax2", torch.float32, 1)
+        _need(state2, "state2", torch.uint8, n, device="state"); _need(absmax2, "absmax2", torch.float32, 1, device="state")
         _need(qmap2, "qmap2", torch.float32, 256)
     if workspace is None:
         workspace = torch.empty(tensorwise_workspace_bytes(), dtype=torch.uint8, device=p.device)
@@ -282,13 +319,13 @@ def step_multi(hp, step, tensors, qmap1=None, qmap2=None, workspace=None, stream
         eight = bool(t.get("is_8bit", True))
         _need(p, "p"); _need(g, "g", p.dtype, n)
         sdt = torch.uint8 if eight else torch.float32
-        _need(t["state1"], "state1", sdt, k * n)
+        _need(t["state1"], "state1", sdt, k * n, device="state")
         if two:
-            _need(t["state2"], "state2", sdt, n)
+            _need(t["state2"], "state2", sdt, n, device="state")
         if eight:
-            _need(t["absmax1"], "absmax1", torch.float32, k * nb)
+            _need(t["absmax1"], "absmax1", torch.float32, k * nb, device="state")
             if two:
-                _need(t["absmax2"], "absmax2", torch.float32, nb)
+                _need(t["absmax2"], "absmax2", torch.float32, nb, device="state")
         arr[i] = Tensor(p.data_ptr(), g.data_ptr(), t["state1"].data_ptr(),
                         t["state2"].data_ptr() if two else None,
                         t["absmax1"].data_ptr() if eight else None,

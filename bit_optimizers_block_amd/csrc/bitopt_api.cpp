@@ -278,6 +278,29 @@ int bitopt_step_32bit_1state(const bitopt_hparams* hp, int32_t step, void* p, co
     return run_step(hp, step, p, g, dtype, n, state1, nullptr, nullptr, nullptr, nullptr, nullptr, false, stream, fn);
 }
 
+int bitopt_host_state_alloc(int64_t bytes, void** ptr) {
+    const char* fn = "bitopt_host_state_alloc";
+    if (!ptr || bytes <= 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: bytes must be > 0 and ptr non-NULL", fn);
+    *ptr = nullptr;
+    void* h = nullptr;
+    hipError_t e = hipHostMalloc(&h, (size_t)bytes, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) return device_status(e, fn);
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess || d != h) {
+        (void)hipHostFree(h);
+        if (e != hipSuccess) return device_status(e, fn);
+        return fail(BITOPT_ERR_UNSUPPORTED, "%s: the device address of pinned host memory differs from its host address", fn);
+    }
+    *ptr = h;
+    return ok();
+}
+
+int bitopt_host_state_free(void* ptr) {
+    if (!ptr) return ok();
+    return device_status(hipHostFree(ptr), "bitopt_host_state_free");
+}
+
 int64_t bitopt_tensorwise_workspace_bytes(void) { return (int64_t)bitopt::tensorwise_workspace_words() * 4; }
 
 int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype,

@@ -185,6 +185,15 @@ def f3_tensorwise_4096(dtype: str = "f32") -> Workload:
                     [Tensor("w", (4096, 4096), dtype, True)], steps=20, p_scale=0.02, g_scale=1e-2)
 
 
+def f4_paged_4096(dtype: str = "f32") -> Workload:
+    """The block-wise AdamW workload with the optimizer state (codes, absmax) kept in
+    pinned host memory instead of HBM ("paged" state)."""
+    w = c2_adamw_4096(dtype, 256)
+    w.name = f"adamw8bit_4096x4096_{dtype}_b256_paged"
+    w.extra = {"paged": True}
+    return w
+
+
 MIN_8BIT_SIZE = 4096
 
 

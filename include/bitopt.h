@@ -250,6 +250,21 @@ BITOPT_API int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t ste
                                            float* absmax1, float* absmax2, const float* qmap1,
                                            const float* qmap2, void* workspace, void* stream);
 
+/*
+ * Optimizer state outside HBM ("paged" state: the optimizer overview's is_paged, the
+ * Paged*8bit optimizers of the 8-bit PR's optimizer table).  Pinned host memory,
+ * mapped into the GPU's address space with the same address, so the state arrays of
+ * any step (codes, absmax, fp32 states) may live there: the kernels read and write it
+ * over the host link instead of HBM, unchanged.  Paging state in or out is a copy
+ * between such a buffer and device memory (e.g. hipMemcpyAsync) between steps.
+ *   bytes  > 0; *ptr receives the address (usable by the host and in every step call)
+ *   Returns BITOPT_ERR_DEVICE if the allocation fails, BITOPT_ERR_UNSUPPORTED if the
+ *   runtime maps it at a different device address.  The memory is caller-owned until
+ *   passed to bitopt_host_state_free (after the last step using it has completed).
+ */
+BITOPT_API int bitopt_host_state_alloc(int64_t bytes, void** ptr);
+BITOPT_API int bitopt_host_state_free(void* ptr);
+
 /* Bytes of device workspace bitopt_step_multi needs for `count` tensors (< 0 if count < 0). */
 BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
 

@@ -178,3 +178,11 @@ def test_tensorwise_argument_errors(B):
     h1 = B.make_hparams(dict(optimizer="rmsprop", blocksize=0))                               # 1-state: no state2
     assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h1), 1, P, P, 0, 0, P, None, P, None, P, None, P, None) == B.OK
     assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 0, P, P, 0, 16, P, P, P, P, P, P, P, None) == E
+
+
+def test_host_state_argument_errors(B):
+    L = B.lib()
+    out = ctypes.c_void_p()
+    assert L.bitopt_host_state_alloc(0, ctypes.byref(out)) == B.ERR_INVALID_ARG
+    assert L.bitopt_host_state_alloc(16, None) == B.ERR_INVALID_ARG
+    assert L.bitopt_host_state_free(None) == B.OK

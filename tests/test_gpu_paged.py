@@ -1,0 +1,102 @@
+"""GPU parity with optimizer state kept outside HBM: the codes and absmax (8-bit)
+or the fp32 states (32-bit) live in pinned host memory mapped into the GPU address
+space (bitopt_host_state_alloc, the library's reading of paged optimizer state);
+the same step kernels read and write them over the host link.  Parameters and
+gradients stay in device memory.  Bar as for the device-resident step."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_optimizers_block_amd import bitopt
+from bit_optimizers_block_amd import workloads as W
+from parity import Compare, Quant8, as_f32, param_rtol, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    bitopt.lib()
+
+
+def _page_out(q):
+    """Move q's state arrays into host_state() memory (same contents)."""
+    for key in ("s1", "s2", "a1", "a2"):
+        t = q.d.get(key)
+        if t is None:
+            continue
+        h = bitopt.host_state(t.numel(), t.dtype)
+        h.copy_(t.cpu())
+        q.d[key] = h
+
+
+CASES = [
+    ("adam", "f32", 256, dict(optimizer="adam", lr=1e-3, weight_decay=0.01)),
+    ("ademamix", "bf16", 256, dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0, t_alpha=3, t_beta3=3)),
+    ("momentum", "f16", 2048, dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01)),
+    ("rmsprop", "f32", 256, dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8)),
+]
+
+
+@pytest.mark.parametrize("name,dtype,bs,hp", CASES, ids=[c[0] for c in CASES])
+def test_paged_state_8bit(name, dtype, bs, hp):
+    n = 7 * 1024 + 300 + 4 if name != "ademamix" else 7 * 1024 + 304
+    hp = dict(hp, blocksize=bs)
+    p0 = W.to_dtype(W.normal_f32([1700, 1], n, 0.02), dtype)
+    q = Quant8(hp, p0, dtype)
+    _page_out(q)
+    assert not q.d["s1"].is_cuda
+    cmp = Compare()
+    for t in range(1, 4):
+        g = W.to_dtype(W.normal_f32([1700, 2, t], n, 0.01), dtype)
+        q.step_gpu(t, to_dev(g, dtype))
+        q.step_oracle(t, g)
+        q.compare(cmp, f"step {t}")
+    print(f"\n[paged {name} {dtype} B{bs}] " + cmp.summary())
+
+
+def test_paged_state_32bit():
+    n = 5000
+    hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01, blocksize=256)
+    p0 = W.normal_f32([1710, 1], n, 0.02)
+    op, os1, os2 = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    dp = to_dev(p0, "f32")
+    ds1, ds2 = bitopt.host_state(n, torch.float32), bitopt.host_state(n, torch.float32)
+    ds1.zero_(); ds2.zero_()
+    for t in range(1, 4):
+        g = W.normal_f32([1710, 2, t], n, 0.01)
+        bitopt.step_32bit_2state(hp, t, dp, to_dev(g, "f32"), ds1, ds2)
+        oracle.step_32bit(hp, t, op, g, "f32", os1, os2)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(dp), op)
+        np.testing.assert_array_equal(ds1.numpy(), os1)
+        np.testing.assert_array_equal(ds2.numpy(), os2)
+
+
+def test_paged_state_tensorwise_and_paging_back():
+    """Tensor-wide step on host state, then the state paged back into HBM (a copy)
+    and stepped there: the trajectory is the one of the oracle throughout."""
+    n = 6000
+    hp = dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01, blocksize=0)
+    p0 = W.normal_f32([1720, 1], n, 0.02)
+    q1 = oracle.dynamic_map(True)
+    o = dict(p=p0.copy(), s1=np.zeros(n, np.uint8), a1=np.zeros(1, np.float32))
+    dp = to_dev(p0, "f32")
+    hs1, ha1 = bitopt.host_state(n), bitopt.host_state(1, torch.float32)
+    hs1.zero_(); ha1.zero_()
+    dq = torch.from_numpy(q1).cuda()
+    ws = None
+    for t in range(1, 5):
+        g = W.normal_f32([1720, 2, t], n, 0.01)
+        if t == 3:                                     # page the state back into device memory
+            torch.cuda.synchronize()
+            hs1, ha1 = hs1.cuda(), ha1.cuda()
+        ws = bitopt.step_8bit_tensorwise(hp, t, dp, to_dev(g, "f32"), hs1, ha1, dq, workspace=ws)
+        oracle.step_8bit(hp, t, o["p"], g, "f32", o["s1"], o["a1"], q1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(dp), o["p"])
+        np.testing.assert_array_equal(hs1.cpu().numpy(), o["s1"])
+        np.testing.assert_array_equal(ha1.cpu().numpy(), o["a1"])
