@@ -675,14 +675,20 @@ __device__ __forceinline__ void load_grad(const StepArgs& a, int64_t base, int l
     }
 }
 
+// Loads complete in issue order, so the inputs a tile consumes first go out first:
+// the states (codes and absmax, or fp32 states), then p -- unless the state update
+// itself reads p (decay folded into the gradient), when p goes first.
+template <int OPT> struct StateReadsP {
+    static constexpr bool v = OPT == kMomentum || OPT == kRmsprop || OPT == kAdagrad;
+};
+
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
-__device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int lane,
-                                          TileRaw<DT, OPT, BS, QUANT>& r) {
+__device__ __forceinline__ void load_params(const StepArgs& a, int64_t base, int lane,
+                                            TileRaw<DT, OPT, BS, QUANT>& r) {
     using L = Layout<BS>;
     using R = TileRaw<DT, OPT, BS, QUANT>;
     using Raw4 = typename Elem<DT>::Raw4;
     using T = typename Elem<DT>::T;
-    const int64_t blk0 = base / BS;
 #pragma unroll
     for (int q = 0; q < R::NQ; ++q) {
         if (SKIP && !((r.live >> (q / L::QPB)) & 1u)) continue;          // wave-uniform
@@ -690,6 +696,15 @@ __device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int l
 #pragma unroll
         for (int i = 0; i < R::PW; ++i) r.p[q][i] = pv[i];
     }
+}
+
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
+__device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int lane,
+                                          TileRaw<DT, OPT, BS, QUANT>& r) {
+    using L = Layout<BS>;
+    using R = TileRaw<DT, OPT, BS, QUANT>;
+    const int64_t blk0 = base / BS;
+    if constexpr (StateReadsP<OPT>::v) load_params<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
 #pragma unroll
     for (int k = 0; k < R::NS; ++k) {
         const int slot = Slot<OPT>::which(k);
@@ -716,6 +731,7 @@ __device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int l
             for (int b = 0; b < R::BPT; ++b) r.A[k][b] = 0.0f;
         }
     }
+    if constexpr (!StateReadsP<OPT>::v) load_params<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
 }
 
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP>

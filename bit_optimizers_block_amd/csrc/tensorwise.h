@@ -26,11 +26,6 @@ constexpr int kTwWordsPerPart = 4;         // max bits of up to three states, no
 constexpr int kTwMaxParts = 1024;          // groups of pass 1 (grid-stride beyond)
 constexpr int kTwWords = kTwHead + kTwWordsPerPart * kTwMaxParts;
 
-// State updates that read the parameter (weight decay folded into the gradient).
-template <int OPT> struct StateNeedsP {
-    static constexpr bool v = OPT == kMomentum || OPT == kRmsprop || OPT == kAdagrad;
-};
-
 // One quad of lane l of a tile: element indices e .. e+3 (FULL: in range and aligned).
 template <int DT, int OPT, bool SKIP, bool FULL, bool NEEDP>
 __device__ __forceinline__ void tw_quad(const StepArgs& a, const float* const (&Q)[2], const float (&A)[3],
@@ -94,7 +89,7 @@ __device__ __forceinline__ void tw_old_absmax(const StepArgs& a, float (&A)[3]) 
 template <int DT, int OPT, bool SKIP>
 __global__ __launch_bounds__(kThreads) void k_tw_max(StepArgs a) {
     constexpr int NS = NumStates<OPT>::v;
-    constexpr bool NEEDP = StateNeedsP<OPT>::v;
+    constexpr bool NEEDP = StateReadsP<OPT>::v;
     constexpr int NMAPS = (OPT == kAdam || OPT == kAdemamix) ? 2 : 1;
     __shared__ float Q1[256], Q2[256];
     Q1[threadIdx.x] = gbl(a.q1)[threadIdx.x];
