@@ -144,8 +144,10 @@ hipError_t dispatch_step(const bitopt::StepArgs& a, int opt, int dtype, int bs, 
     }
 }
 
-// Elements per wave tile of the step kernels (Layout<BS>::TE).
-int64_t tile_elems(int32_t blocksize) { return blocksize >= 1024 ? blocksize : 1024; }
+// Elements per wave tile of the step kernels.
+int64_t tile_elems(int32_t blocksize) {
+    return blocksize == 256 ? bitopt::Layout<256>::TE : bitopt::Layout<2048>::TE;
+}
 
 bool vec_ok(const bitopt_hparams* hp, const void* p, const void* g, int32_t dtype, int64_t n,
             const void* s1, const void* s2) {

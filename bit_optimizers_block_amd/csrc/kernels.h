@@ -537,7 +537,7 @@ __device__ __forceinline__ void block_absmax_lanes(const float (&m)[BPT], float&
 template <int BPT>
 __device__ __forceinline__ float block_value(float v, int b) {
     if constexpr (BPT == 1) return v;
-    else return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * b));
+    else return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (64 / BPT) * b));
 }
 
 // The same as uniform per-block values.
