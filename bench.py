@@ -87,6 +87,19 @@ def workload_bytes(wl) -> float:
     return total
 
 
+def skip_aware_bytes(wl, g_dev, full_bytes):
+    """With skip_zeros, a block whose gradients are all zero needs only its gradient
+    read: the algorithmic bytes of a step over gradient g."""
+    t = wl.tensors[0]
+    n, B = t.numel, wl.hp["blocksize"]
+    nbk = (n + B - 1) // B
+    pad = torch.zeros(nbk * B, device=g_dev.device)
+    pad[:n] = g_dev.float().abs()
+    live = int((pad.view(nbk, B).amax(1) > 0).sum().item())
+    gsz = {"f32": 4, "f16": 2, "bf16": 2}[t.dtype]
+    return full_bytes * live / nbk + gsz * B * (nbk - live)
+
+
 class Model:
     """Device buffers of every tensor of a multi-tensor workload, stepped with one
     bitopt_step_multi call (one launch per tensor kind)."""
@@ -350,6 +363,8 @@ def profile(workload: str, outdir: str, steps: int):
     wl = workload_by_name(workload)
     t = wl.tensors[0]
     alg = workload_bytes(wl)
+    if wl.hp.get("skip_zeros"):
+        alg = skip_aware_bytes(wl, Replica(wl, 0, torch.device("cuda:0")).g, alg)
     d = {"workload": workload, "kernel": kname, "source_hash": source_hash(),
          "kernel_trace_calls": calls, "kernel_trace_avg_us": avg_ns / 1e3,
          "fetch_kib_per_launch": sum(fs) / len(fs), "write_kib_per_launch": sum(ws) / len(ws),
@@ -425,14 +440,7 @@ def main():
         reps = [Replica(wl, r, dev) for r in range(args.replicas)]
         launchers = None
         if hp.get("skip_zeros"):
-            # a block whose gradients are all zero needs only its gradient read
-            g = reps[0].g.float()
-            nbk = (n + B - 1) // B
-            pad = torch.zeros(nbk * B, device=dev)
-            pad[:n] = g.abs()
-            live = int((pad.view(nbk, B).amax(1) > 0).sum().item())
-            gsz = {"f32": 4, "f16": 2, "bf16": 2}[t.dtype]
-            step_bytes = step_bytes * live / nbk + gsz * B * (nbk - live)
+            step_bytes = skip_aware_bytes(wl, reps[0].g, step_bytes)
     torch.cuda.synchronize()
 
     step_no = 0
