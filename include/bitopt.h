@@ -276,7 +276,10 @@ BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
  * launches.  A device table of the group's tensors is written into `workspace`
  * (device, at least bitopt_multi_workspace_bytes(count) bytes, 16-byte aligned) by
  * an asynchronous copy on `stream`; the host array `tensors` may be reused as soon
- * as the call returns.  Work on one workspace must stay in stream order.
+ * as the call returns.  Work on one workspace must stay in stream order.  The copy
+ * reads host memory owned by the call, so this entry point is not meant for capture
+ * into a HIP graph (the per-tensor and tensor-wide steps are: they enqueue kernels
+ * only).
  *   tensors   host array of count descriptors (n == 0 entries are skipped)
  *   qmap1/2   device codebooks as for the per-tensor calls (needed when any
  *             tensor is 8-bit; qmap2 for 2-state optimizers)

@@ -1,0 +1,74 @@
+"""GPU: the per-tensor and tensor-wide steps captured into a HIP graph (through
+torch.cuda.graph) and replayed several times -- with eager work and synchronisation
+between the replays -- give, replay after replay, exactly the result of the same
+calls made eagerly.  The steps enqueue kernels only (no memset or copy nodes)."""
+import numpy as np
+import pytest
+import torch
+
+from bit_optimizers_block_amd import bitopt
+from bit_optimizers_block_amd import workloads as W
+from parity import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    bitopt.lib()
+
+
+def _state(n, nb, two, k=1):
+    return dict(s1=torch.zeros(k * n, dtype=torch.uint8, device="cuda"), a1=torch.zeros(k * nb, device="cuda"),
+                s2=torch.zeros(n, dtype=torch.uint8, device="cuda") if two else None,
+                a2=torch.zeros(nb, device="cuda") if two else None)
+
+
+def _compare(a, b, what):
+    for key in a:
+        if a[key] is not None:
+            np.testing.assert_array_equal(to_host(a[key]), to_host(b[key]), err_msg=f"{what} {key}")
+
+
+@pytest.mark.parametrize("mode", ["blockwise", "tensorwise"])
+def test_captured_step_replays_like_eager(mode):
+    n = 3 * 4096 + 77
+    bs = 0 if mode == "tensorwise" else 256
+    hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01, blocksize=bs)
+    nb = 1 if bs == 0 else (n + bs - 1) // bs
+    p0 = W.normal_f32([1800, 1], n, 0.02)
+    g = to_dev(W.normal_f32([1800, 2], n, 0.01), "f32")
+    q1, q2 = bitopt.create_dynamic_map(True).cuda(), bitopt.create_dynamic_map(False).cuda()
+    A = dict(p=to_dev(p0, "f32"), **_state(n, nb, True))        # stepped by the graph
+    B = dict(p=to_dev(p0, "f32"), **_state(n, nb, True))        # stepped eagerly
+    ws = {"A": torch.empty(bitopt.tensorwise_workspace_bytes(), dtype=torch.uint8, device="cuda"),
+          "B": torch.empty(bitopt.tensorwise_workspace_bytes(), dtype=torch.uint8, device="cuda")}
+
+    def step(S, key):
+        if mode == "tensorwise":
+            bitopt.step_8bit_tensorwise(hp, 1, S["p"], g, S["s1"], S["a1"], q1, S["s2"], S["a2"], q2,
+                                        workspace=ws[key])
+        else:
+            bitopt.step_8bit_blockwise_2state(hp, 1, S["p"], g, S["s1"], S["s2"], S["a1"], S["a2"], q1, q2)
+
+    # warm the step up on a side stream (as torch.cuda.graph expects), then capture it
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        C = dict(p=to_dev(p0, "f32"), **_state(n, nb, True))
+        step(C, "A")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(A, "A")
+    torch.cuda.synchronize()
+    for r in range(4):
+        graph.replay()
+        step(B, "B")
+        scratch = torch.randn(1 << 20, device="cuda").sum()      # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        _compare(A, B, f"replay {r}")

@@ -19,6 +19,8 @@ OPTS = {
     "ademamix": dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0, t_alpha=3, t_beta3=3),
     "momentum": dict(optimizer="momentum", lr=0.01, beta1=0.9, weight_decay=0.01),
     "lion": dict(optimizer="lion", lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.01),
+    "rmsprop": dict(optimizer="rmsprop", lr=0.01, beta1=0.9, eps=1e-8, weight_decay=0.01),
+    "adagrad": dict(optimizer="adagrad", lr=0.01, eps=1e-10, weight_decay=0.01),
 }
 # (n, dtype, is_8bit)
 SPECS = [(5000, "f32", True), (4096, "bf16", True), (70000, "f16", True), (2048, "f32", False),
