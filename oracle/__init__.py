@@ -41,7 +41,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.build(force=False)
+        # BITOPT_ORACLE_LIB: a separately built oracle (the mutation test of the pins
+        # loads deliberately broken builds this way, each in its own process)
+        path = os.environ.get("BITOPT_ORACLE_LIB") or _build.build(force=False)
         L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int32

@@ -16,12 +16,13 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fno-strict
           "-fopenmp", "-fPIC", "-shared", "-fvisibility=hidden", "-Wall", "-Wextra"]
 
 
-def build(force: bool = True, extra_flags=(), out: str = LIB) -> str:
-    """Compile the oracle; returns the path of the shared library."""
-    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+def build(force: bool = True, extra_flags=(), out: str = LIB, src: str = SRC) -> str:
+    """Compile the oracle (or another source, e.g. a mutant in a test); returns the
+    path of the shared library."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
         return out
     tmp = out + ".tmp"
-    cmd = ["gcc", *CFLAGS, *extra_flags, SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", *CFLAGS, *extra_flags, src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
