@@ -63,12 +63,13 @@ def workload_by_name(name):
 NUM_STATES = {"adam": 2, "adamw": 2, "ademamix": 3, "momentum": 1, "lion": 1, "rmsprop": 1, "adagrad": 1}
 
 
-def tensorwise_bytes_per_element(dtype: str, optimizer: str) -> float:
+def tensorwise_bytes_per_element(dtype: str, optimizer: str, max_unorm: float = 0.0) -> float:
     """The two-pass tensor-wide step: pass 1 reads g, the codes and (when the state
-    update uses it) p; pass 2 reads and writes like the block-wise step."""
+    update uses it, or with max_unorm) p; pass 2 reads and writes like the block-wise
+    step."""
     ps = {"f32": 4, "f16": 2, "bf16": 2}[dtype]
     ns = NUM_STATES[optimizer]
-    needs_p = optimizer in ("momentum", "rmsprop", "adagrad")
+    needs_p = optimizer in ("momentum", "rmsprop", "adagrad") or max_unorm > 0.0
     return (3 * ps + 2 * ns) + (ps + ns + (ps if needs_p else 0))
 
 
@@ -78,7 +79,7 @@ def workload_bytes(wl) -> float:
     total = 0.0
     for t in wl.tensors:
         if t.eightbit and wl.hp["blocksize"] == 0:
-            total += tensorwise_bytes_per_element(t.dtype, wl.hp["optimizer"]) * t.numel
+            total += tensorwise_bytes_per_element(t.dtype, wl.hp["optimizer"], wl.hp.get("max_unorm", 0.0)) * t.numel
         elif t.eightbit:
             total += W.bytes_per_element(t.dtype, ns, wl.hp["blocksize"]) * t.numel
         else:   # 32-bit states: read+write p, read g, read+write each fp32 state

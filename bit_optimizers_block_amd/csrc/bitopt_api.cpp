@@ -316,8 +316,6 @@ int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p,
     bitopt_hparams h = *hp;
     h.blocksize = 256;                         // the shared checks know block sizes only
     if (int rc = check_hparams(&h, step, n, fn)) return rc;
-    if (hp->max_unorm > 0.0f)
-        return fail(BITOPT_ERR_UNSUPPORTED, "%s: max_unorm is not supported by the tensor-wide step", fn);
     if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
     if (n == 0) return ok();

@@ -1222,10 +1222,19 @@ __device__ __forceinline__ void step_one_tile_skip(const StepArgs& a, float* Q1,
     }
 }
 
+// Minimum resident waves per SIMD asked of the register allocator.  The 8-bit
+// AdEMAMix step on 16-bit parameters (three states, the most arithmetic per byte)
+// fits five waves without spilling and runs faster there than at four; every other
+// instantiation keeps the allocator's own choice.
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM> struct MinWaves {
+    static constexpr int v = (OPT == kAdemamix && DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM) ? 5 : 1;
+};
+
 // One launch of the fused step: a single tensor (MULTI false: the launch arguments)
 // or every tensor of a descriptor table (MULTI true).
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MinWaves<DT, OPT, BS, QUANT, SKIP, UNORM>::v)))
+void k_step(StepArgs a) {
     constexpr int NMAPS = (OPT == kAdam || OPT == kAdemamix) ? 2 : 1;
     __shared__ float Q1[256], Q2[256], T1[256], T2[256];
     __shared__ __attribute__((aligned(16))) uint8_t B1[search::kNB];

@@ -10,9 +10,14 @@
 //            overwrite the absmax array);
 //   pass 2   reads everything again, recomputes the same values, writes p, encodes
 //            the states with the tensor-wide scale and writes the codes and absmax.
+// With max_unorm (UNORM), pass 1 also reads p and sums the squares of the update and
+// of the parameters (fp32 squares, double sums), the reduction turns the two sums
+// into the tensor's clip factor, and pass 2 scales every update by it.
 // Workspace words: [0, 3) new absmax bits per state, [3, 6) old absmax, [6] nonzero
-// gradient seen; then kTwWordsPerPart words per group of pass 1 (a maximum of
-// non-negative floats is taken on their bit patterns as integers).
+// gradient seen, [7] clip factor (1 when the norm is within the cap); then
+// kTwWordsPerPart words per group of pass 1: the max bits of up to three states, the
+// nonzero-gradient flag and the two sums as double bit patterns split into word
+// pairs (a maximum of non-negative floats is taken on their bit patterns as integers).
 // The element arithmetic is update_elem / apply_step / encode of kernels.h, so the
 // results equal one block spanning the tensor.
 #pragma once
@@ -22,7 +27,7 @@
 namespace bitopt {
 
 constexpr int kTwHead = 8;                 // words before the per-group slots
-constexpr int kTwWordsPerPart = 4;         // max bits of up to three states, nonzero-gradient flag
+constexpr int kTwWordsPerPart = 8;         // 3 max bits, nonzero-gradient flag, 2 x double sum
 constexpr int kTwMaxParts = 1024;          // groups of pass 1 (grid-stride beyond)
 constexpr int kTwWords = kTwHead + kTwWordsPerPart * kTwMaxParts;
 
@@ -85,11 +90,21 @@ __device__ __forceinline__ void tw_old_absmax(const StepArgs& a, float (&A)[3]) 
     }
 }
 
-// Pass 1: the tensor-wide max |new state| of each state.
-template <int DT, int OPT, bool SKIP>
+__device__ __forceinline__ void tw_put_f64(uint32_t* w, double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    w[0] = (uint32_t)b;
+    w[1] = (uint32_t)(b >> 32);
+}
+__device__ __forceinline__ double tw_get_f64(const uint32_t* w) {
+    return __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
+}
+
+// Pass 1: the tensor-wide max |new state| of each state (UNORM: and the sums of
+// squares of the update and of the parameters).
+template <int DT, int OPT, bool SKIP, bool UNORM>
 __global__ __launch_bounds__(kThreads) void k_tw_max(StepArgs a) {
     constexpr int NS = NumStates<OPT>::v;
-    constexpr bool NEEDP = StateReadsP<OPT>::v;
+    constexpr bool NEEDP = StateReadsP<OPT>::v || UNORM;
     constexpr int NMAPS = (OPT == kAdam || OPT == kAdemamix) ? 2 : 1;
     __shared__ float Q1[256], Q2[256];
     Q1[threadIdx.x] = gbl(a.q1)[threadIdx.x];
@@ -104,6 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_tw_max(StepArgs a) {
     const int64_t ntiles = (a.n + 1023) / 1024;
     float mx[3] = {0.0f, 0.0f, 0.0f};
     uint32_t anyl = 0;
+    double su = 0.0, sp = 0.0;
     for (int64_t t = wave_id(); t < ntiles; t += stride) {
         const bool full = a.vec && (t + 1) * 1024 <= a.n;
 #pragma unroll
@@ -118,10 +134,21 @@ __global__ __launch_bounds__(kThreads) void k_tw_max(StepArgs a) {
             for (int k = 0; k < NS; ++k)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx[k] = fmaxf(mx[k], fabsf(st[k][i]));
+            if constexpr (UNORM) {
+                // skipped and out-of-range elements have a zero update, and
+                // out-of-range ones a zero parameter: they add nothing
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float d2 = dl[i] * dl[i];
+                    const float p2 = pv[i] * pv[i];
+                    su += (double)d2;
+                    sp += (double)p2;
+                }
+            }
         }
     }
     // this group's slot: per-wave results through LDS, one lane writes
-    __shared__ uint32_t part[kWavesPerGroup][kTwWordsPerPart];
+    __shared__ uint32_t part[kWavesPerGroup][4];
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -130,35 +157,78 @@ __global__ __launch_bounds__(kThreads) void k_tw_max(StepArgs a) {
     }
     const bool any = wave_any(anyl != 0u);
     if (lane == 0) part[wave][3] = any ? 1u : 0u;
+    __shared__ double sums[kWavesPerGroup][2];
+    if constexpr (UNORM) {
+        su = wave_sum_f64(su);
+        sp = wave_sum_f64(sp);
+        if (lane == 0) { sums[wave][0] = su; sums[wave][1] = sp; }
+    }
     __syncthreads();
-    if (threadIdx.x < kTwWordsPerPart) {
+    uint32_t* slot = a.ws + kTwHead + kTwWordsPerPart * blockIdx.x;
+    if (threadIdx.x < 4) {
         uint32_t v = 0;
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w) v = max(v, part[w][threadIdx.x]);
-        a.ws[kTwHead + kTwWordsPerPart * blockIdx.x + threadIdx.x] = v;
+        slot[threadIdx.x] = v;
+    } else if (threadIdx.x < 6) {
+        const int j = threadIdx.x - 4;
+        double v = 0.0;
+        if constexpr (UNORM) {
+#pragma unroll
+            for (int w = 0; w < kWavesPerGroup; ++w) v += sums[w][j];
+        }
+        tw_put_f64(slot + 4 + 2 * j, v);
     }
 }
 
-// Fold the pass-1 slots into the tensor-wide results; copy the old absmax.
-template <int OPT>
+// Fold the pass-1 slots into the tensor-wide results; copy the old absmax.  UNORM:
+// the clip factor, max_unorm * P / U when U > max_unorm * P (U, P: the norms of the
+// update and of the parameters), else 1.  The sums are folded in a fixed order, so
+// the result does not depend on timing.
+template <int OPT, bool UNORM>
 __global__ __launch_bounds__(kThreads) void k_tw_reduce(StepArgs a) {
     constexpr int NS = NumStates<OPT>::v;
-    __shared__ uint32_t red[kWavesPerGroup][kTwWordsPerPart];
-    uint32_t v[kTwWordsPerPart] = {0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x; i < a.parts; i += kThreads)
+    __shared__ uint32_t red[kWavesPerGroup][4];
+    __shared__ double sums[kWavesPerGroup][2];
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+    double su = 0.0, sp = 0.0;
+    for (int i = threadIdx.x; i < a.parts; i += kThreads) {
+        const uint32_t* slot = a.ws + kTwHead + kTwWordsPerPart * i;
 #pragma unroll
-        for (int j = 0; j < kTwWordsPerPart; ++j) v[j] = max(v[j], a.ws[kTwHead + kTwWordsPerPart * i + j]);
+        for (int j = 0; j < 4; ++j) v[j] = max(v[j], slot[j]);
+        if constexpr (UNORM) {
+            su += tw_get_f64(slot + 4);
+            sp += tw_get_f64(slot + 6);
+        }
+    }
 #pragma unroll
-    for (int j = 0; j < kTwWordsPerPart; ++j) {
+    for (int j = 0; j < 4; ++j) {
         const uint32_t w = __float_as_uint(wave_max_nonneg(__uint_as_float(v[j])));
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][j] = w;
     }
+    if constexpr (UNORM) {
+        su = wave_sum_f64(su);
+        sp = wave_sum_f64(sp);
+        if ((threadIdx.x & 63) == 0) { sums[threadIdx.x >> 6][0] = su; sums[threadIdx.x >> 6][1] = sp; }
+    }
     __syncthreads();
-    if (threadIdx.x < kTwWordsPerPart) {
+    if (threadIdx.x < 4) {
         uint32_t r = 0;
 #pragma unroll
         for (int w = 0; w < kWavesPerGroup; ++w) r = max(r, red[w][threadIdx.x]);
         a.ws[threadIdx.x < 3 ? threadIdx.x : 6] = r;
+    }
+    if (threadIdx.x == 4) {
+        float clip = 1.0f;
+        if constexpr (UNORM) {
+            double tu = 0.0, tp = 0.0;
+#pragma unroll
+            for (int w = 0; w < kWavesPerGroup; ++w) { tu += sums[w][0]; tp += sums[w][1]; }
+            const double U = sqrt(tu), P = sqrt(tp);
+            const double lim = (double)a.s.max_unorm * P;
+            if (U > lim) clip = (float)(lim / U);
+        }
+        a.ws[7] = __float_as_uint(clip);
     }
     if (threadIdx.x < NS) {
         float A[3];
@@ -168,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_tw_reduce(StepArgs a) {
 }
 
 // Pass 2: recompute, write p, encode with the tensor-wide scale, write codes and absmax.
-template <int DT, int OPT, bool SKIP>
+template <int DT, int OPT, bool SKIP, bool UNORM>
 __global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
     constexpr int NS = NumStates<OPT>::v;
     constexpr int NMAPS = (OPT == kAdam || OPT == kAdemamix) ? 2 : 1;
@@ -187,6 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
         const float An = k < NS ? __uint_as_float(a.ws[k]) : 0.0f;
         block_recip(An, r[k], c[k]);
     }
+    const float clip = UNORM ? __uint_as_float(a.ws[7]) : 1.0f;
     const int lane = threadIdx.x & 63;
     if (blockIdx.x == 0 && threadIdx.x < NS) {
         const int k = threadIdx.x;
@@ -204,6 +275,10 @@ __global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
             uint32_t livem;
             if (full) tw_quad<DT, OPT, SKIP, true, true>(a, Q, A, e, pv, st, dl, livem);
             else tw_quad<DT, OPT, SKIP, false, true>(a, Q, A, e, pv, st, dl, livem);
+            if constexpr (UNORM) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dl[i] = dl[i] * clip;   // x * 1 == x: no clip, same bits
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) pv[i] = ((livem >> i) & 1u) ? apply_step<OPT>(a.s, pv[i], dl[i]) : pv[i];
             if (full) {

@@ -5,7 +5,7 @@
 namespace bitopt {
 namespace {
 
-template <int DT, int OPT, bool SKIP>
+template <int DT, int OPT, bool SKIP, bool UNORM>
 hipError_t tw_launch(const StepArgs& a0, hipStream_t s) {
     StepArgs a = a0;
     const dim3 grid = tile_grid(a.n, 1024);
@@ -13,15 +13,17 @@ hipError_t tw_launch(const StepArgs& a0, hipStream_t s) {
     int64_t parts = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
     if (parts > kTwMaxParts) parts = kTwMaxParts;
     a.parts = (int32_t)parts;
-    hipLaunchKernelGGL((k_tw_max<DT, OPT, SKIP>), dim3((unsigned)parts), dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL((k_tw_reduce<OPT>), dim3(1), dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL((k_tw_apply<DT, OPT, SKIP>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_tw_max<DT, OPT, SKIP, UNORM>), dim3((unsigned)parts), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_tw_reduce<OPT, UNORM>), dim3(1), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_tw_apply<DT, OPT, SKIP, UNORM>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 template <int DT, int OPT>
 hipError_t tw_skip(const StepArgs& a, bool skip, hipStream_t s) {
-    return skip ? tw_launch<DT, OPT, true>(a, s) : tw_launch<DT, OPT, false>(a, s);
+    const bool unorm = a.s.max_unorm > 0.0f;
+    if (skip) return unorm ? tw_launch<DT, OPT, true, true>(a, s) : tw_launch<DT, OPT, true, false>(a, s);
+    return unorm ? tw_launch<DT, OPT, false, true>(a, s) : tw_launch<DT, OPT, false, false>(a, s);
 }
 
 template <int OPT>

@@ -232,17 +232,19 @@ typedef struct bitopt_tensor {
  * to measure that claim.  The same update, codes and maps as the block-wise steps:
  *   absmax1  device fp32, 1 entry (AdEMAMix: 2, m1's then m2's)
  *   state2, absmax2 (1 entry), qmap2  2-state optimizers; NULL for 1-state ones
- *   hp->blocksize must be 0 (one block spanning the tensor); hp->max_unorm > 0 gives
- *            BITOPT_ERR_UNSUPPORTED (no per-tensor norm pass)
+ *   hp->blocksize must be 0 (one block spanning the tensor); hp->max_unorm > 0 caps
+ *            the norm of the whole tensor's update at max_unorm times the norm of
+ *            its parameters (one block of n elements)
  *   workspace device memory of at least bitopt_tensorwise_workspace_bytes() bytes,
  *            4-byte aligned, caller-owned and overwritten; calls that may run
  *            concurrently must not share one
  * The new absmax depends on every element, so the step is three launches on
- * `stream`: a pass that reads g, the codes and (Momentum, RMSprop, Adagrad) p and
- * leaves each group's max |new state| in the workspace; a one-group reduction of
- * those; a pass that reads everything again, writes p, encodes with the
- * tensor-wide scale and writes codes and absmax.  The results equal the
- * block-wise step with one block of n elements (deterministic: no atomics).
+ * `stream`: a pass that reads g, the codes and (Momentum, RMSprop, Adagrad, or
+ * with max_unorm) p and leaves each group's max |new state| (and sums of squares of
+ * update and parameters) in the workspace; a one-group reduction of those; a pass
+ * that reads everything again, writes p, encodes with the tensor-wide scale and
+ * writes codes and absmax.  The results equal the block-wise step with one block
+ * of n elements (deterministic: no atomics).
  */
 BITOPT_API int64_t bitopt_tensorwise_workspace_bytes(void);
 BITOPT_API int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g,

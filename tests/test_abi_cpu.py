@@ -167,9 +167,10 @@ def test_tensorwise_argument_errors(B):
     hb = B.make_hparams(dict(optimizer="adam", blocksize=256))
     assert L.bitopt_step_8bit_tensorwise(ctypes.byref(hb), 1, P, P, 0, 16, P, P, P, P, P, P, P, None) == E
     assert "blocksize" in B.last_error()
-    hu = B.make_hparams(dict(optimizer="adam", blocksize=0, max_unorm=1.0))
-    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(hu), 1, P, P, 0, 16, P, P, P, P, P, P, P, None) == \
-        B.ERR_UNSUPPORTED
+    hu = B.make_hparams(dict(optimizer="adam", blocksize=0, max_unorm=1.0))             # tensor-wide cap: accepted
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(hu), 1, P, P, 0, 0, P, P, P, P, P, P, P, None) == B.OK
+    hn = B.make_hparams(dict(optimizer="adam", blocksize=0, max_unorm=-1.0))
+    assert L.bitopt_step_8bit_tensorwise(ctypes.byref(hn), 1, P, P, 0, 16, P, P, P, P, P, P, P, None) == E
     assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 1, P, P, 0, 16, P, P, P, P, P, P, None, None) == E
     assert "NULL" in B.last_error()
     assert L.bitopt_step_8bit_tensorwise(ctypes.byref(h), 1, P, P, 0, 16, P, None, P, P, P, P, P, None) == E

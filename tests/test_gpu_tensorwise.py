@@ -81,9 +81,9 @@ def _grad(seed, t, n, dtype, zero_frac=0.0):
     return W.to_dtype(g, dtype)
 
 
-def _run(name, n, dtype, steps, seed, zero_frac=0.0, maps=None, skip=False):
-    hp = dict(OPTS[name], skip_zeros=skip)
-    print(f"\n[tensorwise] {name} {dtype} n={n} steps={steps} skip={skip}", flush=True)
+def _run(name, n, dtype, steps, seed, zero_frac=0.0, maps=None, skip=False, max_unorm=0.0):
+    hp = dict(OPTS[name], skip_zeros=skip, max_unorm=max_unorm)
+    print(f"\n[tensorwise] {name} {dtype} n={n} steps={steps} skip={skip} max_unorm={max_unorm}", flush=True)
     q = TW8(hp, W.to_dtype(W.normal_f32([seed, 1], n, 0.02), dtype), dtype, maps)
     cmp = Compare()
     for t in range(1, steps + 1):
@@ -104,6 +104,24 @@ def test_tensorwise_step(name, dtype):
 @pytest.mark.parametrize("name", list(OPTS))
 def test_tensorwise_skip_zeros(name):
     _run(name, 3 * 1024 + 77 if name != "ademamix" else 3 * 1024 + 80, "f16", 3, 1200, zero_frac=0.3, skip=True)
+
+
+@pytest.mark.parametrize("name", list(OPTS))
+def test_tensorwise_max_unorm(name):
+    """A cap of 0.002 clips every optimizer's first steps here; the clip factor comes
+    from norms over the whole tensor."""
+    _run(name, 5 * 1024 + 300 + 5 if name != "ademamix" else 5 * 1024 + 304, "f32", 3, 1700, max_unorm=0.002)
+
+
+def test_tensorwise_max_unorm_skip_f16_and_off():
+    _run("adam", 3 * 1024 + 77, "f16", 3, 1710, zero_frac=0.3, skip=True, max_unorm=0.002)
+    _run("momentum", 2 * 1024 + 5, "f32", 2, 1720, max_unorm=1e30)      # a cap never reached
+
+
+def test_tensorwise_max_unorm_many_groups():
+    """More tiles than pass-1 groups (each group strides over several tiles) and a
+    ragged tail: the partial sums of every group reach the clip factor."""
+    _run("adam", 4100 * 1024 + 3, "f32", 1, 1730, max_unorm=0.002)
 
 
 def test_tensorwise_skip_all_zero_is_noop():

@@ -66,7 +66,7 @@ def _run32(oref, hp, p, gs, dtype="f32"):
 
 
 def _new8(oref, hp, n):
-    B = hp.get("blocksize", 256)
+    B = hp.get("blocksize", 256) or n          # blocksize 0: one block spanning the tensor
     nb = (n + B - 1) // B
     opt = hp["optimizer"]
     st = dict(state1=np.zeros(2 * n if opt == "ademamix" else n, np.uint8),
@@ -524,10 +524,14 @@ def test_skip_zeros_32bit_states_untouched(oref, name):
 
 # ----------------------------------------------------------------------------- max_unorm
 
+@pytest.mark.parametrize("B", [256, 0])
 @pytest.mark.parametrize("name", ["adam", "momentum", "lion", "ademamix", "rmsprop", "adagrad"])
-def test_max_unorm(oref, name):
-    n, B = 256 * 12 + 5, 256
+def test_max_unorm(oref, name, B):
+    """Per block (B = 0: over the whole tensor) the update norm is capped at max_unorm
+    times the parameter norm, keeping its direction."""
+    n = 256 * 12 + 5
     hp = dict(OPT_HP[name], blocksize=B, weight_decay=0.0)
+    B = B or n
     p0 = W.normal_f32([51, 1], n, 0.02)
     g = W.normal_f32([51, 2], n, 0.01)
     outs = {}
