@@ -55,6 +55,9 @@ def workload_by_name(name):
         "adamw_bf16_tensorwise": lambda: W.f3_tensorwise_4096("bf16"),
         "adamw_fp32_b256_paged": lambda: W.f4_paged_4096("f32"),
         "adam_fp32_256x256": W.c1_adam_256,
+        "adam_fp32_1024x9": W.adam_small_1024x9,
+        "adamw32_fp32_4096": lambda: W.adamw_32bit_4096("f32"),
+        "adamw32_bf16_4096": lambda: W.adamw_32bit_4096("bf16"),
         "gpt_1p3b": W.c5_gpt_1p3b,
     }
     return table[name]()
@@ -151,10 +154,12 @@ class Model:
 
 
 class Replica:
-    """Device buffers of one independent copy of the workload's single tensor."""
+    """Device buffers of one independent copy of the workload's single tensor (8-bit
+    states with their absmax, or fp32 states for the 32-bit step)."""
 
     def __init__(self, wl, r, dev):
         t = wl.tensors[0]
+        self.eightbit = t.eightbit
         self.n = n = t.numel
         hp = wl.hp
         B = hp["blocksize"]
@@ -181,13 +186,19 @@ class Replica:
         else:
             def z(numel, dt):
                 return torch.zeros(numel, dtype=dt, device=dev)
-        self.s1 = z(k1 * n, torch.uint8)
-        self.a1 = z(k1 * nb, torch.float32)
-        self.s2 = z(n, torch.uint8) if self.two else None
-        self.a2 = z(nb, torch.float32) if self.two else None
+        sd = torch.uint8 if self.eightbit else torch.float32
+        self.s1 = z(k1 * n, sd)
+        self.s2 = z(n, sd) if self.two else None
+        self.a1 = z(k1 * nb, torch.float32) if self.eightbit else None
+        self.a2 = z(nb, torch.float32) if (self.two and self.eightbit) else None
 
     def step(self, hp, t, q1, q2):
-        if self.tensorwise:
+        if not self.eightbit:
+            if self.two:
+                bitopt.step_32bit_2state(hp, t, self.p, self.g, self.s1, self.s2)
+            else:
+                bitopt.step_32bit_1state(hp, t, self.p, self.g, self.s1)
+        elif self.tensorwise:
             bitopt.step_8bit_tensorwise(hp, t, self.p, self.g, self.s1, self.a1, q1, self.s2, self.a2,
                                         q2 if self.two else None, workspace=self.ws)
         elif self.two:
@@ -204,7 +215,10 @@ class Replica:
         ptr = lambda x: ctypes.c_void_p(x.data_ptr())
         dt = bitopt.DTYPES[self.p.dtype]
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        if self.tensorwise:
+        if not self.eightbit:
+            f = L.bitopt_step_32bit_2state if self.two else L.bitopt_step_32bit_1state
+            tail = (ptr(self.s1), ptr(self.s2), stream) if self.two else (ptr(self.s1), stream)
+        elif self.tensorwise:
             f = L.bitopt_step_8bit_tensorwise
             opt = lambda x: None if x is None else ptr(x)
             tail = (ptr(self.s1), opt(self.s2), ptr(self.a1), opt(self.a2), ptr(q1),
@@ -244,6 +258,13 @@ def cpu_baseline(wl, target_s=15.0):
         p = W.to_dtype(W.normal_f32([wl.seed, 1, 0, 0], n_all, wl.p_scale, 0, n), t.dtype)
         g = W.to_dtype(W.normal_f32([wl.seed, 2, 0, 0], n_all, wl.g_scale, 0, n), t.dtype)
         nb = 1 if B == 0 else (n + B - 1) // B
+        if not t.eightbit:                             # the 32-bit step: fp32 states, no codec
+            m1 = np.zeros(k1 * n, np.float32)
+            m2 = np.zeros(n, np.float32) if two else None
+            t0 = time.perf_counter()
+            for step in range(1, steps + 1):
+                oracle.step_32bit(hp, step, p, g, t.dtype, m1, m2)
+            return time.perf_counter() - t0
         s1, a1 = np.zeros(k1 * n, np.uint8), np.zeros(k1 * nb, np.float32)
         s2 = np.zeros(n, np.uint8) if two else None
         a2 = np.zeros(nb, np.float32) if two else None

@@ -698,7 +698,7 @@ __device__ __forceinline__ void load_params(const StepArgs& a, int64_t base, int
     }
 }
 
-template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool WITHP = true>
 __device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int lane,
                                           TileRaw<DT, OPT, BS, QUANT>& r) {
     using L = Layout<BS>;
@@ -731,7 +731,7 @@ __device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int l
             for (int b = 0; b < R::BPT; ++b) r.A[k][b] = 0.0f;
         }
     }
-    if constexpr (!StateReadsP<OPT>::v) load_params<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
+    if constexpr (!StateReadsP<OPT>::v && WITHP) load_params<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
 }
 
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
@@ -1222,6 +1222,43 @@ __device__ __forceinline__ void step_one_tile_skip(const StepArgs& a, float* Q1,
     }
 }
 
+// One tile per wave (single tensor, grid covering every tile), no skip_zeros: the
+// gradient and the states of the tile are requested before the maps are staged (p
+// after), so their HBM latency overlaps the staging loads and the barrier.  Used
+// for fp32 parameters at B = 2048 (the largest tile, at four waves per SIMD), where
+// it shortens the step by 4%; at B = 256 and for 16-bit parameters the extra
+// registers held across the staging cost as much as the overlap gains.
+template <int DT, int OPT, int BS, bool QUANT, bool UNORM, int NMAPS>
+__device__ __forceinline__ void step_one_tile(const StepArgs& a, float* Q1, float* Q2, float* T1, float* T2,
+                                              uint8_t* B1, uint8_t* B2, uint32_t* vote) {
+    constexpr int64_t TE = Layout<BS>::TE;
+    const int lane = threadIdx.x & 63;
+    const int64_t t = wave_id();
+    const int64_t ntiles = total_tiles<BS, false>(a);
+    const bool full = t < ntiles && tile_full<BS>(a, t);
+    TileRaw<DT, OPT, BS, QUANT> x;
+    if (full) {
+        load_grad<DT, OPT, BS, QUANT, false>(a, t * TE, lane, x);
+        load_rest<DT, OPT, BS, QUANT, false, false>(a, t * TE, lane, x);
+    }
+    const MapLDS M1{Q1, T1, B1}, M2{Q2, T2, B2};
+    bool fast = true;
+    if constexpr (QUANT) fast = stage_maps<NMAPS, UnsignedState1<OPT>::v>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote);
+    if (t >= ntiles) return;
+    if (full) {
+        if (!QUANT || fast) {
+            if constexpr (!StateReadsP<OPT>::v) load_params<DT, OPT, BS, QUANT, false>(a, t * TE, lane, x);
+            process_tile<DT, OPT, BS, QUANT, false, UNORM, true>(a, M1, M2, t * TE, lane, x);
+        } else {
+            guarded_tile<DT, OPT, BS, QUANT, false, UNORM, false, true>(a, M1, M2, t * TE, lane);
+        }
+    } else if (fast) {
+        guarded_tile<DT, OPT, BS, QUANT, false, UNORM, true, false>(a, M1, M2, t * TE, lane);
+    } else {
+        guarded_tile<DT, OPT, BS, QUANT, false, UNORM, false, false>(a, M1, M2, t * TE, lane);
+    }
+}
+
 // Minimum resident waves per SIMD asked of the register allocator.  The 8-bit
 // AdEMAMix step on 16-bit parameters (three states, the most arithmetic per byte)
 // fits five waves without spilling and runs faster there than at four; every other
@@ -1247,9 +1284,10 @@ void k_step(StepArgs a) {
         for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = tab[i].tile0;
         __syncthreads();
     }
-    if constexpr (SKIP && !MULTI) {
+    if constexpr (!MULTI && (SKIP || (BS == 2048 && DT == kF32))) {
         if ((int64_t)gridDim.x * kWavesPerGroup >= total_tiles<BS, false>(a)) {     // uniform
-            step_one_tile_skip<DT, OPT, BS, QUANT, UNORM, NMAPS>(a, Q1, Q2, T1, T2, B1, B2, vote);
+            if constexpr (SKIP) step_one_tile_skip<DT, OPT, BS, QUANT, UNORM, NMAPS>(a, Q1, Q2, T1, T2, B1, B2, vote);
+            else step_one_tile<DT, OPT, BS, QUANT, UNORM, NMAPS>(a, Q1, Q2, T1, T2, B1, B2, vote);
             return;
         }
     }

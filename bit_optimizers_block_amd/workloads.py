@@ -194,6 +194,20 @@ def f4_paged_4096(dtype: str = "f32") -> Workload:
     return w
 
 
+def adam_small_1024x9() -> Workload:
+    """The pages' small benchmark shape (1024 x 9 fp32, Adam 8-bit), where the step
+    is launch-bound rather than bandwidth-bound."""
+    return Workload("adam8bit_1024x9_fp32_b256", 7, _adam_hp(),
+                    [Tensor("w", (1024, 9), "f32", True)], steps=10, p_scale=0.02, g_scale=1e-2)
+
+
+def adamw_32bit_4096(dtype: str = "f32") -> Workload:
+    """The 32-bit comparator of the block-wise AdamW workload: the same tensor and
+    hyper-parameters with fp32 states (no codec)."""
+    return Workload(f"adamw32bit_4096x4096_{dtype}", 2, _adam_hp(weight_decay=0.01),
+                    [Tensor("w", (4096, 4096), dtype, False)], steps=20, p_scale=0.02, g_scale=1e-2)
+
+
 MIN_8BIT_SIZE = 4096
 
 
