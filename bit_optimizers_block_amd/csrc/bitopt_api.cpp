@@ -97,6 +97,9 @@ bitopt::StepScalars make_scalars(const bitopt_hparams& h, int32_t t) {
     s.omb3 = (float)(1.0 - b3t);
     s.alpha_t = (float)alpha_at((double)h.alpha, t, h.t_alpha);
     s.max_unorm = h.max_unorm;
+    // the root optimizers' denominator then stays below 2^85, so its hardware
+    // reciprocal is a normal number (the error bound of the 16-bit parameter path)
+    s.fast_root = (h.eps <= 0x1p60f && s.rs2 <= 0x1p20f) ? 1 : 0;
     return s;
 }
 
@@ -104,19 +107,19 @@ bitopt::StepScalars make_scalars(const bitopt_hparams& h, int32_t t) {
 
 namespace bitopt {
 
-// Compute units of each device, queried on first use.  Groups per CU: 64 4-wave
-// groups, i.e. one tile per wave up to 16 M elements (B = 256) on 256 CUs, and a
+// Compute units of each device, queried on first use.  Groups per CU: 256 4-wave
+// groups, i.e. one tile per wave up to 64 M elements (B = 256) on 256 CUs, and a
 // grid stride beyond that, so very large launches stage the LDS codebooks once per
-// group for many tiles rather than once per tile.  Measured on MI355X: one tile per
-// wave streams best (the hardware refills CUs as groups retire); the cap matters
-// only for launches of hundreds of millions of elements.
+// group for several tiles rather than once per tile.  Measured on MI355X: one tile
+// per wave streams best (the hardware refills CUs as groups retire); for the 1.3 G
+// element multi-tensor step 256 per CU ran 4% faster than 64 and than 1024.
 int64_t group_cap() {
     constexpr int kMaxDev = 64;
     static std::atomic<int> cus[kMaxDev];
     static const int per_cu = [] {
         const char* e = std::getenv("BITOPT_GROUPS_PER_CU");
         const int v = e ? std::atoi(e) : 0;
-        return v > 0 ? v : 64;
+        return v > 0 ? v : 256;
     }();
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 2048;

@@ -42,6 +42,7 @@ struct StepScalars {
     float omb1, omb2, ic1, rs2, decay;
     float b3t, omb3, alpha_t;
     float max_unorm;
+    int32_t fast_root;   // eps <= 2^60 and rs2 <= 2^20 (see root_delta_estimate)
 };
 
 // One tensor of a multi-tensor launch (device table entry): the same fields as a
@@ -438,6 +439,46 @@ __device__ __forceinline__ float root_delta(const StepScalars& s, float p, float
     return s.lr * u;
 }
 
+// The same parameter step from the hardware estimates: square root and reciprocal
+// each within one ulp (for v outside (0, 2^-96) and a denominator below 2^85, which
+// eps <= 2^60 and rs2 <= 2^20 ensure), so the step differs from root_delta by at most
+// 13 units of 2^-24 relative, plus 2^-140 absolute where it is subnormal.
+template <int OPT>
+__device__ __forceinline__ float root_delta_estimate(const StepScalars& s, float p, float g, const float st[3]) {
+    const float r = __builtin_amdgcn_sqrtf(st[RootState<OPT>::v]);
+    float num, den;
+    if constexpr (OPT == kAdam || OPT == kAdemamix) {
+        den = r * s.rs2;
+        den = den + s.eps;
+        num = st[0] * s.ic1;
+        if constexpr (OPT == kAdemamix) {
+            const float t2 = s.alpha_t * st[1];
+            num = num + t2;
+        }
+    } else {
+        const float t1 = s.wd * p;
+        num = g + t1;
+        den = r + s.eps;
+    }
+    const float u = num * __builtin_amdgcn_rcpf(den);
+    return s.lr * u;
+}
+
+// Whether a new 16-bit parameter z, formed from an estimated step d, rounds to the
+// same 16-bit value as the one formed from the exact step: true when z - m and z + m
+// round alike, m = |d| 2^-19 + |z| 2^-21 + 2^-120 being at least twice the distance
+// the estimate can move z (13 * 2^-24 |d| + 2 * 2^-24 |z| + 2^-140).  Rounding is
+// monotone, so every value between z - m and z + m -- the exact one included --
+// rounds alike.  Non-finite z or m fail.
+template <int DT>
+__device__ __forceinline__ bool rounds_alike(float z, float d) {
+    const float m = __builtin_fmaf(__builtin_fabsf(d), 0x1p-19f, __builtin_fmaf(__builtin_fabsf(z), 0x1p-21f, 0x1p-120f));
+    const float lo = z - m;
+    const float hi = z + m;
+    const uint32_t w = narrow2<DT>(lo, hi);
+    return m < __builtin_inff() && (w & 0xffffu) == (w >> 16);
+}
+
 // One element of one step.  st[] holds the decoded states on entry and the new
 // states on exit; the parameter step delta is returned through d.
 // Adam/AdEMAMix: st = {m, v} / {m1, m2, nu};  Momentum: {buf};  Lion: {m};
@@ -805,12 +846,37 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
 #pragma unroll
             for (int k = 0; k < NS; ++k) st[k][q][i] = live[q][i] ? s3[k] : st[k][q][i];
         }
+        bool applied = false;      // uniform: pf[q] already holds the new parameters
         if constexpr (ROOT) {
             // The unscaled square root is exact unless a second moment of the quad lies
             // in (0, 2^-96); then the quad takes the general one (same bits either way).
             bool tiny = false;
 #pragma unroll
             for (int i = 0; i < 4; ++i) tiny = tiny || sqrt_needs_scaling(st[RootState<OPT>::v][q][i]);
+            const bool any_tiny = wave_any(tiny);
+            if constexpr (EARLY && DT != kF32) {
+                // 16-bit parameters: the step from the hardware estimates gives the
+                // stored parameter whenever the rounding test shows that no error
+                // within the estimate's bound changes its 16-bit rounding; the quad
+                // otherwise recomputes the step exactly (the same bits either way).
+                if (a.s.fast_root && !any_tiny) {
+                    float z[4];
+                    bool unsure = false;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
+                                             NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
+                        const float d = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
+                        z[i] = apply_step<OPT>(a.s, pf[q][i], d);
+                        unsure = unsure || !rounds_alike<DT>(z[i], d);
+                    }
+                    if (!wave_any(unsure)) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pf[q][i] = z[i];
+                        applied = true;
+                    }
+                }
+            }
             auto deltas = [&](auto unscaled) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -820,12 +886,16 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
                     dl[q][i] = live[q][i] ? d : 0.0f;
                 }
             };
-            if (wave_any(tiny)) deltas(std::false_type{});
-            else deltas(std::true_type{});
+            if (!applied) {
+                if (any_tiny) deltas(std::false_type{});
+                else deltas(std::true_type{});
+            }
         }
         if constexpr (EARLY) {
+            if (!applied) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pf[q][i] = apply_step<OPT>(a.s, pf[q][i], dl[q][i]);
+                for (int i = 0; i < 4; ++i) pf[q][i] = apply_step<OPT>(a.s, pf[q][i], dl[q][i]);
+            }
             store4<DT>(a.p, L::elem(base, lane, q), pf[q]);
         }
     }
