@@ -8,15 +8,22 @@
 // fp32 values, evaluating exactly the fp32 comparison the definition makes:
 // (Q[j+1] - x) < (x - Q[j]).  Then code(x) = #{j : tau[j] <= x}.
 //
-// Bucket table.  The fp32 line is cut into buckets by the float's exponent and its
-// top M mantissa bits (clamped to 25 binades, 2^-24 .. 2^1, each sign), and each
-// bucket stores the code at its lower end.  The generator checks that no bucket
-// holds more than one threshold, so on the device
-//     code(x) = bucket[idx(x)] + (x >= tau[bucket[idx(x)]]).
+// Bucket table.  The device looks values up scaled by 2^-kShift (search_layout.h):
+// the fp32 line of y' = x * 2^-kShift is cut into buckets by the low 5 exponent bits
+// and the top kM mantissa bits, each sign, and each bucket stores the code at its
+// lower end.  The thresholds are stored scaled the same way (exact: every |tau| is
+// far above 2^-30).  The generator checks that no bucket holds more than one
+// threshold, so on the device
+//     code(x) = bucket[idx(y')] + (y' >= tau'[bucket[idx(y')]]),
+// and then replays that formula against a brute-force nearest-entry scan on values
+// around every threshold and map entry and on random values; any difference fails
+// the build.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
+#include <random>
 
 #include "dynamic_map.h"
 #include "search_layout.h"
@@ -58,16 +65,80 @@ int code_at(const float* tau, float x) {
     return c;
 }
 
-// Value range [vmin, vmax] of bucket index k.
+// Value range [vmin, vmax] (scaled, y' space) of bucket index k.
 void bucket_range(int k, float* vmin, float* vmax) {
     using namespace bitopt::search;
     const bool neg = k < kNBH;
-    const int b = neg ? (kNBH - 1 - k) : (k - kNBH);          // magnitude sub-bucket
-    const uint32_t key_lo = (uint32_t)(kKLO + b);
-    const uint32_t mag_lo = b == 0 ? 0u : (key_lo << (23 - kM));
-    const uint32_t mag_hi = b == kNBH - 1 ? 0x7f800000u : (((key_lo + 1) << (23 - kM)) - 1);
+    const uint32_t key = (uint32_t)(neg ? (kNBH - 1 - k) : (k - kNBH));
+    const uint32_t mag_lo = key << 16;
+    const uint32_t mag_hi = ((key + 1) << 16) - 1;
     if (!neg) { *vmin = u2f(mag_lo); *vmax = u2f(mag_hi); }
     else { *vmin = -u2f(mag_hi); *vmax = -u2f(mag_lo); }
+}
+
+// The device encoder on a scaled value: bucket, then one threshold comparison.
+int table_code(const uint8_t* table, const float* tau_s, float ys, bool nonneg) {
+    using namespace bitopt::search;
+    const uint32_t bits = f2u(ys);
+    const uint32_t key = (bits >> 16) & (uint32_t)(kNBH - 1);
+    const uint32_t sgn = nonneg ? 0u : (uint32_t)((int32_t)bits >> 31);
+    const uint32_t idx = (uint32_t)kNBH + (key ^ sgn);
+    const int c = table[idx];
+    return c + (ys >= tau_s[c] ? 1 : 0);
+}
+
+int brute_nearest(const float* Q, float x) {
+    int best = 0;
+    float bd = std::fabs(x - Q[0]);
+    for (int j = 1; j < 256; ++j) {
+        const float d = std::fabs(x - Q[j]);
+        if (d < bd) { bd = d; best = j; }
+    }
+    return best;
+}
+
+// x * 2^-kShift rounded once to fp32, as the device's multiply by the scaled
+// reciprocal gives it (exact for |x| >= 2^-30).
+float scaled(float x) { return (float)std::ldexp((double)x, -bitopt::search::kShift); }
+
+// Replay the table encoder against the brute-force scan; returns the mismatch count.
+long verify(const float* Q, const float* tau, const uint8_t* table, const float* tau_s, bool is_signed) {
+    long bad = 0, tested = 0;
+    auto check = [&](float x) {
+        if (!(std::fabs(x) <= 1.0000002f)) return;
+        if (!is_signed && x < 0.0f) return;
+        const int want = brute_nearest(Q, x);
+        for (int nn = 0; nn < (x >= 0.0f && !std::signbit(x) ? 2 : 1); ++nn) {
+            const int got = table_code(table, tau_s, scaled(x), nn == 1);
+            ++tested;
+            if (got != want) {
+                if (bad < 10) std::fprintf(stderr, "gen_tables: x=%a nonneg=%d table %d nearest %d\n", x, nn, got, want);
+                ++bad;
+            }
+        }
+    };
+    for (int j = 0; j < 256; ++j) {
+        const float pts[2] = {Q[j], j < 255 ? tau[j] : Q[j]};
+        for (float c : pts)
+            for (int d = -64; d <= 64; ++d) {
+                const uint32_t u = f2u(c);
+                check(u2f(u + (uint32_t)d));
+                check(-u2f(u + (uint32_t)d));
+            }
+    }
+    std::mt19937 rng(12345);
+    std::uniform_real_distribution<float> uni(-1.0f, 1.0f);
+    std::uniform_real_distribution<float> lg(-40.0f, 0.0f);
+    for (int i = 0; i < 200000; ++i) {
+        check(uni(rng));
+        const float m = (float)std::exp2((double)lg(rng));
+        check(m);
+        check(-m);
+    }
+    const float special[] = {0.0f, -0.0f, 1.0f, -1.0f, 0x1p-30f, 0x1p-31f, 0x1p-126f, 0x1p-149f, 1.0000001f};
+    for (float x : special) check(x);
+    if (tested == 0) return 1;
+    return bad;
 }
 
 void emit_floats(FILE* f, const char* name, const float* v, int n) {
@@ -89,22 +160,34 @@ int main(int argc, char** argv) {
         float Q[256], tau[256];
         bitopt::build_dynamic_map(s == 0, Q);
         thresholds(Q, tau);
+        float tau_s[256];
+        for (int j = 0; j < 256; ++j) tau_s[j] = j < 255 ? (float)std::ldexp((double)tau[j], -kShift) : tau[j];
+        for (int j = 0; j < 255; ++j)
+            if (std::ldexp((double)tau_s[j], kShift) != (double)tau[j] || std::fabs(tau[j]) < 0x1p-30f) {
+                std::fprintf(stderr, "gen_tables: threshold %d of map %d does not scale exactly\n", j, s);
+                return 1;
+            }
         static uint8_t table[kNB];
         for (int k = 0; k < kNB; ++k) {
             float vmin, vmax;
             bucket_range(k, &vmin, &vmax);
-            const int c0 = code_at(tau, vmin), c1 = code_at(tau, vmax);
+            const int c0 = code_at(tau_s, vmin), c1 = code_at(tau_s, vmax);
             if (c1 - c0 > 1) {
                 std::fprintf(stderr, "gen_tables: bucket %d of map %d holds %d thresholds\n", k, s, c1 - c0);
                 return 1;
             }
             table[k] = (uint8_t)c0;
         }
+        const long bad = verify(Q, tau, table, tau_s, s == 0);
+        if (bad) {
+            std::fprintf(stderr, "gen_tables: table encoder disagrees with the nearest entry on %ld values (map %d)\n", bad, s);
+            return 1;
+        }
         char name[64];
         std::snprintf(name, sizeof name, "kStdQ%d", s);
         emit_floats(f, name, Q, 256);
         std::snprintf(name, sizeof name, "kStdTau%d", s);
-        emit_floats(f, name, tau, 256);
+        emit_floats(f, name, tau_s, 256);
         std::fprintf(f, "alignas(16) static __device__ const uint8_t kStdBucket%d[%d] = {", s, kNB);
         for (int k = 0; k < kNB; ++k) std::fprintf(f, "%s%u", k % 24 ? "," : ",\n    " + (k == 0), table[k]);
         std::fprintf(f, "};\n\n");

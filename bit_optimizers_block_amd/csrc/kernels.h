@@ -262,23 +262,32 @@ struct MapLDS {
     const uint8_t* bkt;
 };
 
-// Nearest code of x.  FAST (standard maps): one bucket lookup and one threshold
-// comparison, code = bkt[idx(x)] + (x >= tau[bkt[idx(x)]]), which equals the
-// nearest-entry rule for every finite x.  Otherwise the binary search above.
-template <bool FAST>
+// Nearest code.  FAST (standard maps): x is the normalized value scaled by
+// 2^-kShift (see search_layout.h), and one bucket lookup plus one threshold
+// comparison give code = bkt[idx(x)] + (x >= tau'[bkt[idx(x)]]), equal to the
+// nearest-entry rule for every finite value.  NONNEG: the value is known to be
+// non-negative (a second-moment state), so the sign term of the index is dropped.
+// Otherwise x is the plain normalized value and the binary search above applies.
+template <bool FAST, bool NONNEG = false>
 __device__ __forceinline__ uint32_t encode(const MapLDS& m, float x) {
     if constexpr (FAST) {
         using namespace search;
         const uint32_t bits = __float_as_uint(x);
-        const uint32_t key = (bits >> (23 - kM)) & ((1u << (8 + kM)) - 1u);
-        const uint32_t b = min(max(key, (uint32_t)kKLO), (uint32_t)kKHI) - (uint32_t)kKLO;
-        const uint32_t idx = (uint32_t)kNBH + (b ^ (uint32_t)((int32_t)bits >> 31));
+        const uint32_t key = (bits >> 16) & (uint32_t)(kNBH - 1);
+        const uint32_t idx = (uint32_t)kNBH + (NONNEG ? key : (key ^ (uint32_t)((int32_t)bits >> 31)));
         const uint32_t c = m.bkt[idx];
         return c + (x >= m.tau[c] ? 1u : 0u);
     } else {
         return nearest_code(m.Q, x);
     }
 }
+
+// The table encoder's scale, folded into a block's reciprocal r: r * 2^-kShift.  It
+// gives the scaled value exactly when r >= 2^(kShift - 126) or r == 0; a block with a
+// smaller reciprocal (absmax above 2^30) takes the binary search instead.
+constexpr float kEncScale = 0x1p-96f;
+static_assert(search::kShift == 96 && search::kMinRecipExp == -30, "encoder scale");
+__device__ __forceinline__ bool table_recip_ok(float r) { return !(r < 0x1p-30f); }
 
 // Stage up to two codebooks into LDS.  Map 1 is expected to be the standard signed
 // map (EXP1 = 1: the unsigned one) and map 2 the standard unsigned one, so their
@@ -361,7 +370,7 @@ __device__ __forceinline__ bool stage_maps(const float* q1, const float* q2, flo
 // v - neighbour * estimate shows that neighbour is the rounded root.  This is the
 // general correctly rounded expansion without its input scaling and its final
 // zero/infinity select, and gives the same bits wherever that scaling is not
-// applied; positive v below 2^-96 need the scaling (see sqrt_needs_scaling).
+// applied; positive v below 2^-96 need the scaling (see quad_needs_scaling).
 __device__ __forceinline__ float sqrt_rn_unscaled(float v) {
     const float s = __builtin_amdgcn_sqrtf(v);
     const float dn = __uint_as_float(__float_as_uint(s) - 1u);
@@ -371,9 +380,12 @@ __device__ __forceinline__ float sqrt_rn_unscaled(float v) {
     const float r = rdn <= 0.0f ? dn : s;
     return rup > 0.0f ? up : r;
 }
-// v in (0, 2^-96) (as bits of a non-negative float: 1 .. 0x0F7FFFFF)
-__device__ __forceinline__ bool sqrt_needs_scaling(float v) {
-    return __float_as_uint(v) - 1u < 0x0F7FFFFFu;
+// Whether any of four non-negative values lies in (0, 2^-96), i.e. has bits in
+// 1 .. 0x0F7FFFFF: one unsigned minimum of the bit patterns minus one (0 wraps high).
+__device__ __forceinline__ bool quad_needs_scaling(const float (&v)[4]) {
+    const uint32_t m01 = min(__float_as_uint(v[0]) - 1u, __float_as_uint(v[1]) - 1u);
+    const uint32_t m23 = min(__float_as_uint(v[2]) - 1u, __float_as_uint(v[3]) - 1u);
+    return min(m01, m23) < 0x0F7FFFFFu;
 }
 
 // Optimizers whose step divides by a root of a second-moment state.
@@ -469,14 +481,16 @@ __device__ __forceinline__ float root_delta_estimate(const StepScalars& s, float
 // round alike, m = |d| 2^-19 + |z| 2^-21 + 2^-120 being at least twice the distance
 // the estimate can move z (13 * 2^-24 |d| + 2 * 2^-24 |z| + 2^-140).  Rounding is
 // monotone, so every value between z - m and z + m -- the exact one included --
-// rounds alike.  Non-finite z or m fail.
+// rounds alike.  The margin is returned through m: a non-finite margin (z or d not
+// finite) makes the test void, which the caller checks once for a quad by summing
+// the margins (the sum is finite only if every margin is).
 template <int DT>
-__device__ __forceinline__ bool rounds_alike(float z, float d) {
-    const float m = __builtin_fmaf(__builtin_fabsf(d), 0x1p-19f, __builtin_fmaf(__builtin_fabsf(z), 0x1p-21f, 0x1p-120f));
+__device__ __forceinline__ bool rounds_alike(float z, float d, float& m) {
+    m = __builtin_fmaf(__builtin_fabsf(d), 0x1p-19f, __builtin_fmaf(__builtin_fabsf(z), 0x1p-21f, 0x1p-120f));
     const float lo = z - m;
     const float hi = z + m;
     const uint32_t w = narrow2<DT>(lo, hi);
-    return m < __builtin_inff() && (w & 0xffffu) == (w >> 16);
+    return (w & 0xffffu) == (w >> 16);
 }
 
 // One element of one step.  st[] holds the decoded states on entry and the new
@@ -607,8 +621,10 @@ __device__ __forceinline__ void store_code_word(uint8_t* cp, int64_t e, int64_t 
 }
 
 // Encode the lane's values of one tile: per-block absmax (A, uniform), nearest
-// codes of value * (1/A).  Quads of blocks past the end hold zeros.
-template <int BS, bool FAST, int NQ>
+// codes of value * (1/A).  Quads of blocks past the end hold zeros.  The table
+// encoder serves tiles whose blocks all have a normal absmax of at most 2^30; a
+// tile with a subnormal (prescaled) or larger absmax takes the binary search.
+template <int BS, bool FAST, bool NONNEG, int NQ>
 __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ][4], uint32_t w[NQ],
                                             float (&A)[Layout<BS>::BPT]) {
     using L = Layout<BS>;
@@ -623,24 +639,28 @@ __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ
         m[b] = x;
     }
     block_absmax<L::BPT>(m, A, r, c);
-    bool scaled = false;                            // a subnormal block absmax (uniform)
+    bool table = FAST;                              // uniform
 #pragma unroll
-    for (int b = 0; b < L::BPT; ++b) scaled = scaled || c[b] != 1.0f;
-    auto codes = [&](auto prescale) {
+    for (int b = 0; b < L::BPT; ++b) table = table && c[b] == 1.0f && table_recip_ok(r[b]);
+    if (table) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const float rq = r[q / L::QPB] * kEncScale;
+            uint32_t x = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x |= encode<true, NONNEG>(M, v[q][i] * rq) << (8 * i);
+            w[q] = x;
+        }
+    } else {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const float rq = r[q / L::QPB], cq = c[q / L::QPB];
             uint32_t x = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float y = decltype(prescale)::value ? (v[q][i] * cq) * rq : v[q][i] * rq;
-                x |= encode<FAST>(M, y) << (8 * i);
-            }
+            for (int i = 0; i < 4; ++i) x |= encode<false>(M, (v[q][i] * cq) * rq) << (8 * i);
             w[q] = x;
         }
-    };
-    if (scaled) codes(std::true_type{});
-    else codes(std::false_type{});
+    }
 }
 
 // ---------------------------------------------------------------- fused step tile
@@ -850,17 +870,14 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
         if constexpr (ROOT) {
             // The unscaled square root is exact unless a second moment of the quad lies
             // in (0, 2^-96); then the quad takes the general one (same bits either way).
-            bool tiny = false;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tiny = tiny || sqrt_needs_scaling(st[RootState<OPT>::v][q][i]);
-            const bool any_tiny = wave_any(tiny);
+            const bool any_tiny = wave_any(quad_needs_scaling(st[RootState<OPT>::v][q]));
             if constexpr (EARLY && DT != kF32) {
                 // 16-bit parameters: the step from the hardware estimates gives the
                 // stored parameter whenever the rounding test shows that no error
                 // within the estimate's bound changes its 16-bit rounding; the quad
                 // otherwise recomputes the step exactly (the same bits either way).
                 if (a.s.fast_root && !any_tiny) {
-                    float z[4];
+                    float z[4], mg[4];
                     bool unsure = false;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -868,8 +885,10 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
                                              NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
                         const float d = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
                         z[i] = apply_step<OPT>(a.s, pf[q][i], d);
-                        unsure = unsure || !rounds_alike<DT>(z[i], d);
+                        unsure |= !rounds_alike<DT>(z[i], d, mg[i]);
                     }
+                    const float msum = (mg[0] + mg[1]) + (mg[2] + mg[3]);
+                    unsure |= !(msum < __builtin_inff());
                     if (!wave_any(unsure)) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) pf[q][i] = z[i];
@@ -949,7 +968,10 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
         if constexpr (QUANT) {
             uint32_t w[NQ];
             float A[BPT];
-            encode_tile<BS, FAST>(slot ? M2 : M1, st[k], w, A);
+            if (k == RootState<OPT>::v && HasRoot<OPT>::v)      // a second moment: never negative
+                encode_tile<BS, FAST, true>(slot ? M2 : M1, st[k], w, A);
+            else
+                encode_tile<BS, FAST, false>(slot ? M2 : M1, st[k], w, A);
             float* am = (slot ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
             uint8_t* cp = reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + eo;
 #pragma unroll
@@ -1167,8 +1189,14 @@ __device__ __forceinline__ void guarded_tile(const StepArgs& a, const MapLDS& M1
             if constexpr (QUANT) {
                 const float rb = lane_value(rv[k], qb), cb = lane_value(cv[k], qb);
                 uint32_t w = 0;
+                if (FAST && cb == 1.0f && table_recip_ok(rb)) {       // uniform
+                    const float rs = rb * kEncScale;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w |= encode<FAST>(slot ? M2 : M1, (st[k][i] * cb) * rb) << (8 * i);
+                    for (int i = 0; i < 4; ++i) w |= encode<true>(slot ? M2 : M1, st[k][i] * rs) << (8 * i);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w |= encode<false>(slot ? M2 : M1, (st[k][i] * cb) * rb) << (8 * i);
+                }
                 store_code_word<VEC>(reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + eo, e, n, w);
             } else {
                 float* fp = reinterpret_cast<float*>(slot ? a.s2 : a.s1) + eo;
@@ -1402,7 +1430,7 @@ __device__ __forceinline__ void quant_tile(const CodecArgs& a, const MapLDS& M, 
     }
     uint32_t w[NQ];
     float A[L::BPT];
-    encode_tile<BS, FAST>(M, v, w, A);
+    encode_tile<BS, FAST, false>(M, v, w, A);
 #pragma unroll
     for (int b = 0; b < L::BPT; ++b)
         if ((FULL || blk0 + b < a.nb) && lane == 0) gbl(a.absmax)[blk0 + b] = A[b];

@@ -250,12 +250,15 @@ __global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
     const bool fast = stage_maps<NMAPS, UnsignedState1<OPT>::v>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote);
     const MapLDS M[2] = {MapLDS{Q1, T1, B1}, MapLDS{Q2, T2, B2}};
     const float* const Q[2] = {Q1, Q2};
-    float A[3], r[3], c[3];
+    float A[3], r[3], c[3], rs[3];
+    bool tab[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         A[k] = k < NS ? __uint_as_float(a.ws[3 + k]) : 0.0f;
         const float An = k < NS ? __uint_as_float(a.ws[k]) : 0.0f;
         block_recip(An, r[k], c[k]);
+        tab[k] = fast && c[k] == 1.0f && table_recip_ok(r[k]);
+        rs[k] = r[k] * kEncScale;
     }
     const float clip = UNORM ? __uint_as_float(a.ws[7]) : 1.0f;
     const int lane = threadIdx.x & 63;
@@ -292,10 +295,12 @@ __global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
             for (int k = 0; k < NS; ++k) {
                 const int slot = Slot<OPT>::which(k);
                 uint32_t w = 0;
+                if (tab[k]) {                                       // uniform
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float y = (st[k][i] * c[k]) * r[k];
-                    w |= (fast ? encode<true>(M[slot], y) : encode<false>(M[slot], y)) << (8 * i);
+                    for (int i = 0; i < 4; ++i) w |= encode<true>(M[slot], st[k][i] * rs[k]) << (8 * i);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w |= encode<false>(M[slot], (st[k][i] * c[k]) * r[k]) << (8 * i);
                 }
                 uint8_t* cp = reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + Slot<OPT>::elem_off(k, a.n);
                 if (full) store_code_word<true>(cp, e, a.n, w);

@@ -1,0 +1,99 @@
+"""The device's table encoder, replayed on the CPU against the oracle's nearest code.
+
+The kernels encode a normalized state value y of a standard map through two
+constant tables that the build generates (bucket codes and scaled decision
+thresholds): with y' = y * 2^-96 rounded once to fp32,
+    key = bits(y')[16:28],  idx = 4096 + (key ^ (sign ? ~0 : 0)),
+    code = bucket[idx] + (y' >= tau'[bucket[idx]]),
+and second-moment states (never negative) drop the sign term.  This test reads the
+generated tables and checks that formula element by element against the oracle's
+brute-force nearest-entry scan (the definition: the entry at the least fp32
+distance, ties to the lower index) on values around every threshold and map entry,
+on random values and on the special values -0, 0, +-1 and tiny magnitudes.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_optimizers_block_amd import build as libbuild
+
+SCALE = np.float32(2.0 ** -96)
+
+
+def _tables():
+    path = os.path.join(libbuild.GEN, "bitopt_tables.h")
+    if not os.path.exists(path):
+        libbuild.generate_tables()
+    text = open(path).read()
+
+    def arr(name, dtype):
+        m = re.search(r"\b%s\[(\d+)\] = \{([^}]*)\}" % name, text)
+        assert m, name
+        vals = [int(v.strip().rstrip("u"), 0) for v in m.group(2).split(",") if v.strip()]
+        assert len(vals) == int(m.group(1))
+        return np.array(vals, dtype=dtype)
+
+    out = {}
+    for s in (0, 1):
+        out[s] = dict(Q=arr(f"kStdQ{s}", np.uint32).view(np.float32),
+                      tau=arr(f"kStdTau{s}", np.uint32).view(np.float32),
+                      bkt=arr(f"kStdBucket{s}", np.uint8))
+    return out
+
+
+def table_encode(t, x, nonneg):
+    y = (x.astype(np.float32) * SCALE).astype(np.float32)
+    bits = y.view(np.uint32).astype(np.uint64)
+    key = (bits >> np.uint64(16)) & np.uint64(0xFFF)
+    if nonneg:
+        idx = 4096 + key
+    else:
+        sgn = np.where(bits >> np.uint64(31) != 0, np.uint64(0xFFFFFFFF), np.uint64(0))
+        idx = (np.uint64(4096) + (key ^ sgn)) & np.uint64(0xFFFFFFFF)
+    assert idx.max() < 8192
+    c = t["bkt"][idx.astype(np.int64)].astype(np.int64)
+    with np.errstate(invalid="ignore"):
+        return (c + (y >= t["tau"][c])).astype(np.uint8)
+
+
+def probe_values(Q, tau):
+    pts = np.concatenate([Q, tau[:255]]).astype(np.float32)
+    d = np.arange(-256, 257, dtype=np.int64)
+    around = (pts.view(np.uint32).astype(np.int64)[:, None] + d[None, :]).ravel()
+    around = around[(around >= 0) & (around < 2 ** 32)].astype(np.uint32).view(np.float32)
+    rng = np.random.default_rng(7)
+    uni = rng.uniform(-1.0, 1.0, 400_000).astype(np.float32)
+    mag = np.exp2(rng.uniform(-40.0, 0.0, 200_000)).astype(np.float32)
+    special = np.array([0.0, -0.0, 1.0, -1.0, 2.0 ** -30, 2.0 ** -31, 2.0 ** -126, 2.0 ** -149,
+                        np.nextafter(np.float32(1), np.float32(2))], np.float32)
+    x = np.concatenate([around, -around, uni, mag, -mag, special])
+    return x[np.isfinite(x) & (np.abs(x) <= np.float32(1.0000002))]
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_table_encoder_matches_oracle_nearest(signed):
+    t = _tables()[0 if signed else 1]
+    Q = oracle.dynamic_map(signed)
+    np.testing.assert_array_equal(t["Q"], Q)           # the library's map is the oracle's
+    x = probe_values(Q, t["tau"].astype(np.float32) / SCALE)
+    if not signed:
+        x = x[(x >= 0) & ~np.signbit(x)]
+    want = oracle.nearest(Q, x)
+    got = table_encode(t, x, nonneg=False)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} mismatches, first x={x[bad[0]]!r} got {got[bad[0]]} want {want[bad[0]]}"
+    pos = (x >= 0) & ~np.signbit(x)
+    got_nn = table_encode(t, x[pos], nonneg=True)
+    np.testing.assert_array_equal(got_nn, want[pos])
+
+
+def test_table_encoder_special_inputs_stay_in_range():
+    """Infinities map to the extreme codes; NaN and values beyond the normalized range
+    still index inside the tables (the key needs no clamp)."""
+    t = _tables()[0]
+    x = np.array([np.inf, -np.inf], np.float32)
+    np.testing.assert_array_equal(table_encode(t, x, nonneg=False), [255, 0])
+    table_encode(t, np.array([np.nan, 3.0, -7.5e30, 1e38], np.float32), nonneg=False)   # in range (asserted)
