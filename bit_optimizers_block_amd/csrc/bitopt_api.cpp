@@ -113,14 +113,15 @@ namespace bitopt {
 // group for several tiles rather than once per tile.  Measured on MI355X: one tile
 // per wave streams best (the hardware refills CUs as groups retire); for the 1.3 G
 // element multi-tensor step 256 per CU ran 4% faster than 64 and than 1024.
-int64_t group_cap() {
+int64_t group_cap(int resident_per_cu) {
     constexpr int kMaxDev = 64;
     static std::atomic<int> cus[kMaxDev];
-    static const int per_cu = [] {
+    static const int env_per_cu = [] {
         const char* e = std::getenv("BITOPT_GROUPS_PER_CU");
         const int v = e ? std::atoi(e) : 0;
-        return v > 0 ? v : 256;
+        return v > 0 ? v : 0;
     }();
+    const int per_cu = env_per_cu > 0 ? env_per_cu : (resident_per_cu > 0 ? resident_per_cu : 256);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 2048;
     int c = cus[dev].load(std::memory_order_relaxed);
@@ -129,6 +130,15 @@ int64_t group_cap() {
         cus[dev].store(c, std::memory_order_relaxed);
     }
     return (int64_t)c * per_cu;
+}
+
+int resident_groups_per_cu(const void* kernel) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return n;
 }
 
 }  // namespace bitopt

@@ -1362,7 +1362,7 @@ __device__ __forceinline__ void step_one_tile(const StepArgs& a, float* Q1, floa
 // fits five waves without spilling and runs faster there than at four; every other
 // instantiation keeps the allocator's own choice.
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM> struct MinWaves {
-    static constexpr int v = (OPT == kAdemamix && DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM) ? 5 : 1;
+    static constexpr int v = (OPT == kAdemamix && DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM) ? 5 : ((OPT == kAdam && DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM) ? 6 : 1);
 };
 
 // One launch of the fused step: a single tensor (MULTI false: the launch arguments)

@@ -23,16 +23,22 @@ int tensorwise_workspace_words();
 hipError_t launch_quantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_dequantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 
-// Upper bound on resident-sized grids for the current device: compute units times
-// the groups per CU the step kernels are launched with (queried once per device).
-int64_t group_cap();
+// Upper bound on the grid for the current device: compute units times the groups
+// per CU the step kernels are launched with (CU count queried once per device).
+// resident_per_cu > 0: that many groups per CU (a grid that is resident at once);
+// 0: 256 per CU, i.e. one tile per wave for any tensor of practical size.  The
+// environment variable BITOPT_GROUPS_PER_CU overrides both.
+int64_t group_cap(int resident_per_cu = 0);
+
+// Groups of `kernel` (kThreads threads, static LDS only) resident on one CU.
+int resident_groups_per_cu(const void* kernel);
 
 // Grid for a wave-per-tile kernel over n elements in tiles of `tile` elements:
 // one tile per wave up to group_cap() groups, grid-stride beyond.
-inline dim3 tile_grid(int64_t n, int64_t tile) {
+inline dim3 tile_grid(int64_t n, int64_t tile, int resident_per_cu = 0) {
     const int64_t tiles = (n + tile - 1) / tile;
     int64_t groups = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    const int64_t cap = group_cap();
+    const int64_t cap = group_cap(resident_per_cu);
     if (groups > cap) groups = cap;
     if (groups < 1) groups = 1;
     return dim3((unsigned)groups);
