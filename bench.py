@@ -351,11 +351,16 @@ def profile(workload: str, outdir: str, steps: int):
     profiles/ are these files)."""
     env = dict(os.environ, TMPDIR="/tmp")
     outdir = os.path.abspath(outdir)
-    base = ["--workload", workload, "--steps", str(steps), "--warmup", "3", "--no-cpu-baseline"]
+    # The trace pass is the benchmark's own command (its default warm-up and timed
+    # launches), so the trace's average duration is taken over the same launches the
+    # benchmark times; the counter passes count bytes, which do not depend on clocks,
+    # over `steps` launches.
     cmds = {}
-    cmds["trace"] = _rocprof(base, os.path.join(outdir, "trace"), ["--kernel-trace", "--stats"], env)
-    cmds["fetch"] = _rocprof(base + ["--copy-calibration"], os.path.join(outdir, "fetch"), ["--pmc", "FETCH_SIZE"], env)
-    cmds["write"] = _rocprof(base + ["--copy-calibration"], os.path.join(outdir, "write"), ["--pmc", "WRITE_SIZE"], env)
+    cmds["trace"] = _rocprof(["--workload", workload, "--no-cpu-baseline"], os.path.join(outdir, "trace"),
+                             ["--kernel-trace", "--stats"], env)
+    base = ["--workload", workload, "--steps", str(steps), "--warmup", "3", "--no-cpu-baseline", "--copy-calibration"]
+    cmds["fetch"] = _rocprof(base, os.path.join(outdir, "fetch"), ["--pmc", "FETCH_SIZE"], env)
+    cmds["write"] = _rocprof(base, os.path.join(outdir, "write"), ["--pmc", "WRITE_SIZE"], env)
 
     stats = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")]
     step_stats = [r for r in stats if "k_step" in r["Name"]]
@@ -413,7 +418,8 @@ def profile(workload: str, outdir: str, steps: int):
         f.write(f"| library source hash | {source_hash()} |\n\n")
         f.write(f"Made by `python bench.py --profile <outdir> --workload {workload} --profile-steps {steps}` "
                 "(from the repository root), which runs the three profiler passes below from /tmp with "
-                "TMPDIR=/tmp; raw output stays in the -d directories.\n\n")
+                "TMPDIR=/tmp; raw output stays in the -d directories.  The trace pass is the benchmark's "
+                "default command (1000 warm-up and 1000 timed launches); its average covers all of them.\n\n")
         for k, c in cmds.items():
             f.write(f"- {k}: `{c}`\n")
     print(json.dumps(d))
