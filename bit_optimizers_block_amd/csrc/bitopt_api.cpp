@@ -381,7 +381,7 @@ int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tenso
         return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace missing, too small or not 16-byte aligned", fn);
 
     // Group by kind (is_8bit, dtype), keeping call order inside a group; chunks of
-    // at most kMaxTableTensors tensors form one launch each.
+    // at most kMaxTableTensors tensors and kMaxLaunchTiles tiles form one launch each.
     const int64_t te = tile_elems(hp->blocksize);
     struct Launch { int kind8, dtype; size_t first, count; int64_t tiles; };
     std::vector<bitopt::TensorDesc> table;
@@ -393,7 +393,10 @@ int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tenso
             for (int32_t i = 0; i < count; ++i) {
                 const bitopt_tensor& t = tensors[i];
                 if (t.n == 0 || (t.is_8bit != 0) != (kind8 != 0) || t.dtype != dt) continue;
-                if (L.count == (size_t)bitopt::kMaxTableTensors) {
+                const int64_t tiles_t = (t.n + te - 1) / te;
+                if (tiles_t > bitopt::kMaxLaunchTiles)
+                    return fail(BITOPT_ERR_UNSUPPORTED, "%s: tensor %d: more than 2^32 - 1 tiles", fn, i);
+                if (L.count == (size_t)bitopt::kMaxTableTensors || L.tiles + tiles_t > bitopt::kMaxLaunchTiles) {
                     launches.push_back(L);
                     L = Launch{kind8, dt, table.size(), 0, 0};
                 }
@@ -403,7 +406,7 @@ int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tenso
                 d.n = t.n; d.nb = (t.n + hp->blocksize - 1) / hp->blocksize;
                 d.tile0 = L.tiles;
                 d.vec = vec_ok(hp, t.p, t.g, t.dtype, t.n, t.state1, two ? t.state2 : nullptr) ? 1 : 0;
-                L.tiles += (t.n + te - 1) / te;
+                L.tiles += tiles_t;
                 ++L.count;
                 table.push_back(d);
             }

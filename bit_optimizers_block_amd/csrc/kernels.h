@@ -61,6 +61,7 @@ struct TensorDesc {
     int32_t pad;
 };
 constexpr int kMaxTableTensors = 1024;     // tensors per multi-tensor launch
+constexpr int64_t kMaxLaunchTiles = 0xFFFFFFFFll;   // tiles per multi-tensor launch (uint32 first-tile indices)
 
 struct StepArgs {
     void* p;
@@ -287,7 +288,7 @@ __device__ __forceinline__ uint32_t encode(const MapLDS& m, float x) {
 // smaller reciprocal (absmax above 2^30) takes the binary search instead.
 constexpr float kEncScale = 0x1p-96f;
 static_assert(search::kShift == 96 && search::kMinRecipExp == -30, "encoder scale");
-__device__ __forceinline__ bool table_recip_ok(float r) { return !(r < 0x1p-30f); }
+__device__ __forceinline__ bool table_recip_ok(float r) { return r >= 0x1p-30f || r == 0.0f; }
 
 // Stage up to two codebooks into LDS.  Map 1 is expected to be the standard signed
 // map (EXP1 = 1: the unsigned one) and map 2 the standard unsigned one, so their
@@ -622,8 +623,11 @@ __device__ __forceinline__ void store_code_word(uint8_t* cp, int64_t e, int64_t 
 
 // Encode the lane's values of one tile: per-block absmax (A, uniform), nearest
 // codes of value * (1/A).  Quads of blocks past the end hold zeros.  The table
-// encoder serves tiles whose blocks all have a normal absmax of at most 2^30; a
-// tile with a subnormal (prescaled) or larger absmax takes the binary search.
+// encoder serves every tile whose blocks have an absmax of at most 2^30 (a subnormal
+// absmax with its 2^24 prescale: its scaled reciprocal stays normal); a larger
+// absmax, or a map without tables, takes the binary search -- one element at a time,
+// so that this path, which practical data never reaches, does not raise the kernel's
+// register count.
 template <int BS, bool FAST, bool NONNEG, int NQ>
 __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ][4], uint32_t w[NQ],
                                             float (&A)[Layout<BS>::BPT]) {
@@ -639,25 +643,39 @@ __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ
         m[b] = x;
     }
     block_absmax<L::BPT>(m, A, r, c);
-    bool table = FAST;                              // uniform
+    bool table = FAST, scaled = false;              // uniform
 #pragma unroll
-    for (int b = 0; b < L::BPT; ++b) table = table && c[b] == 1.0f && table_recip_ok(r[b]);
-    if (table) {
+    for (int b = 0; b < L::BPT; ++b) {
+        table = table && table_recip_ok(r[b]);
+        scaled = scaled || c[b] != 1.0f;
+    }
+    auto tables = [&](auto prescale) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const float rq = r[q / L::QPB] * kEncScale;
+            const float rq = r[q / L::QPB] * kEncScale, cq = c[q / L::QPB];
             uint32_t x = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x |= encode<true, NONNEG>(M, v[q][i] * rq) << (8 * i);
+            for (int i = 0; i < 4; ++i) {
+                const float y = decltype(prescale)::value ? (v[q][i] * cq) * rq : v[q][i] * rq;
+                x |= encode<true, NONNEG>(M, y) << (8 * i);
+            }
             w[q] = x;
         }
+    };
+    if (table && !scaled) {
+        tables(std::false_type{});
+    } else if (table) {
+        tables(std::true_type{});
     } else {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const float rq = r[q / L::QPB], cq = c[q / L::QPB];
             uint32_t x = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x |= encode<false>(M, (v[q][i] * cq) * rq) << (8 * i);
+            for (int i = 0; i < 4; ++i) {
+                x |= encode<false>(M, (v[q][i] * cq) * rq) << (8 * i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             w[q] = x;
         }
     }
@@ -1189,10 +1207,10 @@ __device__ __forceinline__ void guarded_tile(const StepArgs& a, const MapLDS& M1
             if constexpr (QUANT) {
                 const float rb = lane_value(rv[k], qb), cb = lane_value(cv[k], qb);
                 uint32_t w = 0;
-                if (FAST && cb == 1.0f && table_recip_ok(rb)) {       // uniform
+                if (FAST && table_recip_ok(rb)) {                      // uniform
                     const float rs = rb * kEncScale;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w |= encode<true>(slot ? M2 : M1, st[k][i] * rs) << (8 * i);
+                    for (int i = 0; i < 4; ++i) w |= encode<true>(slot ? M2 : M1, (st[k][i] * cb) * rs) << (8 * i);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) w |= encode<false>(slot ? M2 : M1, (st[k][i] * cb) * rb) << (8 * i);
@@ -1234,11 +1252,11 @@ __device__ __forceinline__ int64_t wave_id() {
 // first-tile indices staged in LDS.  The table is constant while the kernel runs,
 // so its entries are read through the constant address space (scalar loads).
 #define BITOPT_CONSTANT __attribute__((address_space(4)))
-__device__ __forceinline__ int64_t resolve_tile(const StepArgs& a0, const int64_t* T0, int64_t gt, StepArgs& a) {
+__device__ __forceinline__ int64_t resolve_tile(const StepArgs& a0, const uint32_t* T0, int64_t gt, StepArgs& a) {
     int lo = 0, hi = a0.ntab - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (T0[mid] <= gt) lo = mid; else hi = mid - 1;
+        if ((int64_t)T0[mid] <= gt) lo = mid; else hi = mid - 1;
     }
     const BITOPT_CONSTANT TensorDesc* tab = (const BITOPT_CONSTANT TensorDesc*)a0.table;
     const BITOPT_CONSTANT TensorDesc& d = tab[__builtin_amdgcn_readfirstlane(lo)];
@@ -1258,7 +1276,7 @@ __device__ __forceinline__ int64_t total_tiles(const StepArgs& a) {
 // its loads before any use; latency is hidden by the other waves of the CU.
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool MULTI, bool FAST>
 __device__ __forceinline__ void step_tiles(const StepArgs& a0, const MapLDS& M1, const MapLDS& M2,
-                                           const int64_t* T0) {
+                                           const uint32_t* T0) {
     constexpr int64_t TE = Layout<BS>::TE;
     // the binary-search encoder runs on the quad-at-a-time path (see guarded_tile)
     constexpr bool WHOLE = !QUANT || FAST;
@@ -1357,12 +1375,15 @@ __device__ __forceinline__ void step_one_tile(const StepArgs& a, float* Q1, floa
     }
 }
 
-// Minimum resident waves per SIMD asked of the register allocator.  The 8-bit
-// AdEMAMix step on 16-bit parameters (three states, the most arithmetic per byte)
-// fits five waves without spilling and runs faster there than at four; every other
-// instantiation keeps the allocator's own choice.
+// Minimum resident waves per SIMD asked of the register allocator, for the 8-bit
+// steps on 16-bit parameters at B = 256 without skip_zeros or max_unorm: AdEMAMix
+// (three states) five, Adam six, Momentum and Lion eight -- each the most that fits
+// without spilling, and measured faster than the allocator's own choice (AdEMAMix
+// at six spills and runs 15% slower).  Every other instantiation keeps the
+// allocator's choice.
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM> struct MinWaves {
-    static constexpr int v = (OPT == kAdemamix && DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM) ? 5 : ((OPT == kAdam && DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM) ? 6 : 1);
+    static constexpr bool hot16 = DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM;
+    static constexpr int v = !hot16 ? 1 : OPT == kAdemamix ? 5 : OPT == kAdam ? 6 : (OPT == kMomentum || OPT == kLion) ? 8 : 1;
 };
 
 // One launch of the fused step: a single tensor (MULTI false: the launch arguments)
@@ -1375,11 +1396,11 @@ void k_step(StepArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t B1[search::kNB];
     __shared__ __attribute__((aligned(16))) uint8_t B2[search::kNB];
     __shared__ uint32_t vote[kWavesPerGroup];
-    __shared__ int64_t T0[MULTI ? kMaxTableTensors : 1];
+    __shared__ uint32_t T0[MULTI ? kMaxTableTensors : 1];   // first tiles (< 2^32 per launch)
     const MapLDS M1{Q1, T1, B1}, M2{Q2, T2, B2};
     if constexpr (MULTI) {
         const BITOPT_CONSTANT TensorDesc* tab = (const BITOPT_CONSTANT TensorDesc*)a.table;
-        for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = tab[i].tile0;
+        for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = (uint32_t)tab[i].tile0;
         __syncthreads();
     }
     if constexpr (!MULTI && (SKIP || (BS == 2048 && DT == kF32))) {

@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
         A[k] = k < NS ? __uint_as_float(a.ws[3 + k]) : 0.0f;
         const float An = k < NS ? __uint_as_float(a.ws[k]) : 0.0f;
         block_recip(An, r[k], c[k]);
-        tab[k] = fast && c[k] == 1.0f && table_recip_ok(r[k]);
+        tab[k] = fast && table_recip_ok(r[k]);
         rs[k] = r[k] * kEncScale;
     }
     const float clip = UNORM ? __uint_as_float(a.ws[7]) : 1.0f;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void k_tw_apply(StepArgs a) {
                 uint32_t w = 0;
                 if (tab[k]) {                                       // uniform
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w |= encode<true>(M[slot], st[k][i] * rs[k]) << (8 * i);
+                    for (int i = 0; i < 4; ++i) w |= encode<true>(M[slot], (st[k][i] * c[k]) * rs[k]) << (8 * i);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) w |= encode<false>(M[slot], (st[k][i] * c[k]) * r[k]) << (8 * i);
