@@ -108,6 +108,56 @@ def test_step_8bit_tiny_second_moments():
         print(f"\n[tiny v {name} {dtype}] " + cmp.summary())
 
 
+def test_step_8bit_huge_states():
+    """Gradient blocks scaled so far up that the new state's block absmax exceeds 2^30:
+    the table encoder's scaled reciprocal would leave the normal range there, so those
+    blocks take the binary search, next to ordinary blocks, in full and ragged tiles."""
+    for name, dtype, big in (("adam", "f32", 1e12), ("momentum", "f32", 1e12), ("lion", "bf16", 1e14)):
+        n, B = RAGGED[256], 256
+        hp = dict(OPTS[name], blocksize=B)
+        p0 = W.to_dtype(W.normal_f32([975, 1], n, 0.02), dtype)
+        q = Quant8(hp, p0, dtype)
+        cmp = Compare()
+        nb = (n + B - 1) // B
+        for t in range(1, 4):
+            g = W.normal_f32([975, 2, t], n, 0.01)
+            scale = np.ones(n, np.float32)
+            for b in list(range(1, nb, 4)) + [nb - 1]:      # includes the ragged last block
+                scale[b * B:(b + 1) * B] = big
+            g = W.to_dtype(g * scale, dtype)
+            q.step_gpu(t, to_dev(g, dtype))
+            q.step_oracle(t, g)
+            q.compare(cmp, f"{name} step {t}")
+        assert np.any(q.o["a1"] > 2.0 ** 30), "no block reached an absmax above 2^30"
+        print(f"\n[huge states {name} {dtype}] " + cmp.summary())
+        assert cmp.bit_exact, cmp.summary()
+
+
+@pytest.mark.parametrize("bs", [256, 2048])
+def test_codec_absmax_around_2_pow_30(bs):
+    """Block absmax just below, at and above 2^30 (the table encoder's limit) and up to
+    the top of the fp32 range, next to ordinary and all-zero blocks."""
+    n = RAGGED[bs]
+    nb = (n + bs - 1) // bs
+    x = W.normal_f32([915, bs], n, 1.0)
+    targets = [2.0 ** 29, 2.0 ** 30, 2.0 ** 30 * (1 + 2.0 ** -23), 2.0 ** 31, 1e20, 2.0 ** 126, 3.0e38, 0.0]
+    for b in range(nb):
+        blk = x[b * bs:(b + 1) * bs]
+        tgt = targets[(b * (3 if bs == 2048 else 1)) % len(targets)]
+        blk *= np.float32(tgt / float(np.abs(blk).max())) if tgt > 0 else np.float32(0.0)
+        if tgt > 0:
+            blk[int(np.argmax(np.abs(blk)))] = np.float32(tgt)          # the exact absmax
+    for signed in (True, False):
+        xs = x if signed else np.abs(x)
+        qmap = oracle.dynamic_map(signed)
+        codes_ref, absmax_ref = oracle.quantize_blockwise(xs, "f32", qmap, bs)
+        codes, absmax = bitopt.quantize_blockwise(to_dev(xs, "f32"), bitopt.create_dynamic_map(signed).cuda(), bs)
+        cmp = Compare()
+        cmp.codes(to_host(codes), codes_ref, "codes")
+        cmp.values(to_host(absmax), absmax_ref, 1e-6, "absmax", kind="a")
+        assert cmp.bit_exact, cmp.summary()
+
+
 def _jittered_map(signed, seed):
     """A sorted 256-entry map close to a standard one but equal to neither standard
     map, so the kernels take the binary-search encoder."""
