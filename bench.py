@@ -345,6 +345,13 @@ def _csv_rows(outdir, suffix):
     return rows
 
 
+def kernel_is_8bit(kname: str) -> bool:
+    """Whether a step kernel's name (k_step<dtype, optimizer, blocksize, 8-bit, ...>)
+    is the 8-bit instantiation."""
+    args = kname[kname.index("<") + 1:kname.index(">")].split(",")
+    return args[3].strip() == "true"
+
+
 def profile(workload: str, outdir: str, steps: int):
     """Kernel trace plus FETCH_SIZE and WRITE_SIZE passes (each its own run) of the
     benchmark; writes <workload>.md and .json into outdir (the summaries kept under
@@ -363,14 +370,17 @@ def profile(workload: str, outdir: str, steps: int):
     cmds["write"] = _rocprof(base, os.path.join(outdir, "write"), ["--pmc", "WRITE_SIZE"], env)
 
     stats = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")]
-    step_stats = [r for r in stats if "k_step" in r["Name"]]
+    # the dominant step kernel (a multi-tensor step launches one kernel per tensor kind)
+    step_stats = sorted((r for r in stats if "k_step" in r["Name"]), key=lambda r: -float(r["TotalDurationNs"]))
     kname = step_stats[0]["Name"]
     avg_ns = float(step_stats[0]["AverageNs"])
     calls = int(step_stats[0]["Calls"])
 
     def counter(name, sub):
         rows = [r for r in _csv_rows(os.path.join(outdir, sub), "counter_collection.csv") if r["Counter_Name"] == name]
-        step = [float(r["Counter_Value"]) for r in rows if "k_step" in r["Kernel_Name"]]
+        step = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == kname]
+        if not step:      # names spelled differently in the two outputs: any step kernel
+            step = [float(r["Counter_Value"]) for r in rows if "k_step" in r["Kernel_Name"]]
         # the calibration copy is the runtime's device-to-device blit kernel: the
         # dispatches of it with the largest grid
         blits = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
@@ -388,7 +398,10 @@ def profile(workload: str, outdir: str, steps: int):
     fetch_b = sum(fs) / len(fs) * f_scale * 1024.0
     write_b = sum(ws) / len(ws) * w_scale * 1024.0
     wl = workload_by_name(workload)
-    t = wl.tensors[0]
+    if len(wl.tensors) > 1:
+        # only the tensors of the dominant kernel's kind (8-bit or 32-bit states)
+        quant = kernel_is_8bit(kname)
+        wl = W.Workload(**{**wl.__dict__, "tensors": [t for t in wl.tensors if t.eightbit == quant]})
     alg = workload_bytes(wl)
     if wl.hp.get("skip_zeros"):
         alg = skip_aware_bytes(wl, Replica(wl, 0, torch.device("cuda:0")).g, alg)
