@@ -105,8 +105,8 @@ def skip_aware_bytes(wl, g_dev, full_bytes):
 
 
 class Model:
-    """Device buffers of every tensor of a multi-tensor workload, stepped with one
-    bitopt_step_multi call (one launch per tensor kind)."""
+    """Device buffers of every tensor of a multi-tensor workload: one plan built up
+    front, each step one bitopt_step_multi_planned call (one launch per tensor kind)."""
 
     def __init__(self, wl, dev):
         import ctypes
@@ -135,19 +135,29 @@ class Model:
         self.count = len(wl.tensors)
         self.ws = torch.empty(bitopt.multi_workspace_bytes(self.count), dtype=torch.uint8, device=dev)
         self.n = sum(t.numel for t in wl.tensors)
+        # the descriptor table is written once (bitopt_multi_plan_build); each step is
+        # then kernel launches only (bitopt_step_multi_planned)
+        self.plan = bitopt.MultiPlanC()
+        h = bitopt.make_hparams(hp)
+        rc = bitopt.lib().bitopt_multi_plan_build(ctypes.byref(h), arr, self.count, ctypes.c_void_p(self.ws.data_ptr()),
+                                                  self.ws.numel(), ctypes.byref(self.plan),
+                                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise bitopt.BitoptError(rc, bitopt.last_error())
+        self.launches_per_step = self.plan.nlaunch
 
     def launcher(self, hp, q1, q2):
         import ctypes
         L = bitopt.lib()
         h = bitopt.make_hparams(hp)
         self._keep = h
-        f = L.bitopt_step_multi
+        f = L.bitopt_step_multi_planned
+        plan = ctypes.byref(self.plan)
         args = (ctypes.c_void_p(q1.data_ptr()), ctypes.c_void_p(q2.data_ptr()),
-                ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
 
         def launch(t):
-            rc = f(ctypes.byref(h), t, self.arr, self.count, *args)
+            rc = f(plan, ctypes.byref(h), t, *args)
             if rc != 0:
                 raise bitopt.BitoptError(rc, bitopt.last_error())
         return launch
@@ -240,11 +250,26 @@ class Replica:
         return launch
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, target_s=15.0):
-    """The oracle, as it stands, on a bounded sample of the same workload: a prefix
-    of the tensor (whole blocks) when one pass over all of it would exceed the
-    target time, else repeated full steps until about target_s seconds."""
+    """The oracle, as it stands, on a bounded sample of the same workload.  A single
+    tensor: a prefix of it (whole blocks) when one pass over all of it would exceed
+    the target time, else repeated full steps until about target_s seconds.  A
+    multi-tensor workload: every small (32-bit) tensor in full plus a prefix of each
+    8-bit tensor, in the workload's proportions of 8-bit and 32-bit elements."""
     import oracle
+    if len(wl.tensors) > 1:
+        return cpu_baseline_multi(wl, target_s)
     t = wl.tensors[0]
     hp = wl.hp
     B = hp["blocksize"]
@@ -286,7 +311,53 @@ def cpu_baseline(wl, target_s=15.0):
     dt = run(n, steps)
     what = "the whole tensor" if n == n_all else f"the first {n} elements ({n // B} blocks of {B})"
     return {"value": n * steps / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{what} of the same workload, {steps} step(s), {dt:.1f} s on {threads} threads"}
+
+
+def cpu_baseline_multi(wl, target_s=15.0):
+    import oracle
+    hp = wl.hp
+    B = hp["blocksize"]
+    threads = oracle.get_threads()
+    two = hp["optimizer"] in ("adam", "adamw", "ademamix")
+    k1 = 2 if hp["optimizer"] == "ademamix" else 1
+    q1, q2 = oracle.dynamic_map(True), oracle.dynamic_map(False)
+    big = [(i, t) for i, t in enumerate(wl.tensors) if t.eightbit]
+    small = [(i, t) for i, t in enumerate(wl.tensors) if not t.eightbit]
+
+    def run(per_tensor_blocks):
+        total, secs = 0, 0.0
+        for i, t in big:
+            n = min(t.numel, per_tensor_blocks * B)
+            p = W.to_dtype(W.normal_f32([wl.seed, 1, i], t.numel, wl.p_scale, 0, n), t.dtype)
+            g = W.to_dtype(W.normal_f32([wl.seed, 2, i, 1], t.numel, wl.g_scale, 0, n), t.dtype)
+            nb = (n + B - 1) // B
+            s1, a1 = np.zeros(k1 * n, np.uint8), np.zeros(k1 * nb, np.float32)
+            s2 = np.zeros(n, np.uint8) if two else None
+            a2 = np.zeros(nb, np.float32) if two else None
+            t0 = time.perf_counter()
+            oracle.step_8bit(hp, 1, p, g, t.dtype, s1, a1, q1, s2, a2, q2 if two else None)
+            secs += time.perf_counter() - t0
+            total += n
+        for i, t in small:
+            n = t.numel
+            p = W.to_dtype(W.normal_f32([wl.seed, 1, i], n, wl.p_scale), t.dtype)
+            g = W.to_dtype(W.normal_f32([wl.seed, 2, i, 1], n, wl.g_scale), t.dtype)
+            m1 = np.zeros(k1 * n, np.float32)
+            m2 = np.zeros(n, np.float32) if two else None
+            t0 = time.perf_counter()
+            oracle.step_32bit(hp, 1, p, g, t.dtype, m1, m2)
+            secs += time.perf_counter() - t0
+            total += n
+        return total, secs
+
+    n0, dt0 = run(16)                                  # calibration
+    blocks = max(16, int(16 * target_s / max(dt0, 1e-6)))
+    n, dt = run(blocks)
+    return {"value": n / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"one step over {len(big)} 8-bit tensors (the first {blocks} blocks of {B} of each) and the "
+                      f"{len(small)} 32-bit tensors in full ({n} elements), {dt:.1f} s on {threads} threads"}
 
 
 def source_hash() -> str:
@@ -352,10 +423,11 @@ def kernel_is_8bit(kname: str) -> bool:
     return args[3].strip() == "true"
 
 
-def profile(workload: str, outdir: str, steps: int):
+def profile(workload: str, outdir: str, steps: int, counter_groups=()):
     """Kernel trace plus FETCH_SIZE and WRITE_SIZE passes (each its own run) of the
-    benchmark; writes <workload>.md and .json into outdir (the summaries kept under
-    profiles/ are these files)."""
+    benchmark, and one more run per group of extra counters (e.g. SQ_INSTS_VALU);
+    writes <workload>.md and .json into outdir (the summaries kept under profiles/
+    are these files)."""
     env = dict(os.environ, TMPDIR="/tmp")
     outdir = os.path.abspath(outdir)
     # The trace pass is the benchmark's own command (its default warm-up and timed
@@ -368,6 +440,9 @@ def profile(workload: str, outdir: str, steps: int):
     base = ["--workload", workload, "--steps", str(steps), "--warmup", "3", "--no-cpu-baseline", "--copy-calibration"]
     cmds["fetch"] = _rocprof(base, os.path.join(outdir, "fetch"), ["--pmc", "FETCH_SIZE"], env)
     cmds["write"] = _rocprof(base, os.path.join(outdir, "write"), ["--pmc", "WRITE_SIZE"], env)
+    base_nc = [a for a in base if a != "--copy-calibration"]
+    for gi, group in enumerate(counter_groups):
+        cmds[f"counters{gi}"] = _rocprof(base_nc, os.path.join(outdir, f"counters{gi}"), ["--pmc", *group], env)
 
     stats = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")]
     # the dominant step kernel (a multi-tensor step launches one kernel per tensor kind)
@@ -405,12 +480,29 @@ def profile(workload: str, outdir: str, steps: int):
     alg = workload_bytes(wl)
     if wl.hp.get("skip_zeros"):
         alg = skip_aware_bytes(wl, Replica(wl, 0, torch.device("cuda:0")).g, alg)
+    kelems = sum(t.numel for t in wl.tensors)
+    extra = {}
+    for gi, group in enumerate(counter_groups):
+        rows = _csv_rows(os.path.join(outdir, f"counters{gi}"), "counter_collection.csv")
+        for name in group:
+            per = {}
+            for r in rows:
+                if r["Counter_Name"] != name or "k_step" not in r["Kernel_Name"]:
+                    continue
+                if r["Kernel_Name"] != kname and any(x["Kernel_Name"] == kname for x in rows):
+                    continue
+                key = r.get("Dispatch_Id", str(len(per)))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            vals = [per[k] for k in sorted(per, key=lambda k: int(k) if k.isdigit() else 0)][-steps:]
+            if vals:
+                extra[name] = sum(vals) / len(vals)
     d = {"workload": workload, "kernel": kname, "source_hash": source_hash(),
          "kernel_trace_calls": calls, "kernel_trace_avg_us": avg_ns / 1e3,
          "fetch_kib_per_launch": sum(fs) / len(fs), "write_kib_per_launch": sum(ws) / len(ws),
          "copy_calibration": {"bytes_each_way": COPY_ELEMS * 4, "fetch_kib": sum(fc) / len(fc),
                               "write_kib": sum(wc) / len(wc), "fetch_scale": f_scale, "write_scale": w_scale},
          "traffic_bytes_per_launch": fetch_b + write_b, "algorithmic_bytes_per_launch": alg,
+         "kernel_elements": kelems, "counters_per_launch": extra,
          "commands": cmds}
     with open(os.path.join(outdir, f"{workload}.json"), "w") as f:
         json.dump(d, f, indent=1)
@@ -429,8 +521,16 @@ def profile(workload: str, outdir: str, steps: int):
         f.write(f"| HBM traffic per launch (scaled) | {(fetch_b + write_b) / 1e6:.1f} MB "
                 f"({(fetch_b + write_b) / alg:.3f} x algorithmic) |\n")
         f.write(f"| library source hash | {source_hash()} |\n\n")
-        f.write(f"Made by `python bench.py --profile <outdir> --workload {workload} --profile-steps {steps}` "
-                "(from the repository root), which runs the three profiler passes below from /tmp with "
+        if extra:
+            f.write("| counter | per launch | per element (x64 for per-wave counts) |\n|---|---|---|\n")
+            for name, v in extra.items():
+                wave = name.startswith("SQ_INSTS") or name in ("SQ_LDS_BANK_CONFLICT", "SQ_WAVES")
+                per_el = v * 64 / kelems if wave else v / kelems
+                f.write(f"| {name} | {v:.6g} | {per_el:.4g} |\n")
+            f.write(f"\nElements updated by the kernel per launch: {kelems}.\n\n")
+        pc = f" --profile-counters '{';'.join(','.join(g) for g in counter_groups)}'" if counter_groups else ""
+        f.write(f"Made by `python bench.py --profile <outdir> --workload {workload} --profile-steps {steps}{pc}` "
+                "(from the repository root), which runs the profiler passes below from /tmp with "
                 "TMPDIR=/tmp; raw output stays in the -d directories.  The trace pass is the benchmark's "
                 "default command (1000 warm-up and 1000 timed launches); its average covers all of them.\n\n")
         for k, c in cmds.items():
@@ -455,9 +555,12 @@ def main():
                     help="run the benchmark under rocprofv3 (kernel trace, FETCH_SIZE, WRITE_SIZE); "
                          "raw output and the <workload>.md/.json summaries go to OUTDIR")
     ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--profile-counters", default="",
+                    help="extra counter passes for --profile: groups separated by ';', counters by ','")
     args = ap.parse_args()
     if args.profile:
-        profile(args.workload, args.profile, args.profile_steps)
+        groups = [[c for c in g.split(",") if c] for g in args.profile_counters.split(";") if g.strip()]
+        profile(args.workload, args.profile, args.profile_steps, groups)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the optimizer step is per-rank local (blocks are independent), "
@@ -527,21 +630,25 @@ def main():
     value = n * args.steps / (total_ms / 1e3) / 1e9
     achieved = step_bytes / (avg_ms / 1e3) / 1e9
 
+    # the parameter dtype of the workload (element arithmetic is fp32, states are u8 codes)
+    dtype = "+".join(sorted({t.dtype for t in wl.tensors}, key=lambda d: -sum(
+        x.numel for x in wl.tensors if x.dtype == d)))
     if multi:
         cfg = {"workload": wl.name, "optimizer": hp["optimizer"], "tensors": len(wl.tensors),
                "params": n, "eightbit_params": sum(t.numel for t in wl.tensors if t.eightbit),
                "param_dtype": "bf16 (8-bit states), f32 (32-bit states)", "blocksize": B,
-               "launches_per_step": 2}
+               "launches_per_step": model.launches_per_step, "arithmetic": "f32", "state_dtype": "u8"}
     else:
         cfg = {"workload": wl.name, "optimizer": hp["optimizer"], "shape": list(t.shape),
                "param_dtype": t.dtype, "blocksize": B, "weight_decay": hp.get("weight_decay", 0.0),
-               "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps)}
+               "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps),
+               "arithmetic": "f32", "state_dtype": "u8" if t.eightbit else "f32"}
         if wl.extra.get("paged"):
             cfg["state_memory"] = "pinned host (paged)"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gelem/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(avg_ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
         "config": cfg,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -553,7 +660,7 @@ def main():
                      "host_us_per_launch": round(host_us, 2)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not multi:
+    if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

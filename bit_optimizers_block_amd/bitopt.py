@@ -74,6 +74,22 @@ class Tensor(ctypes.Structure):
     ]
 
 
+class MultiLaunch(ctypes.Structure):
+    """Mirror of bitopt_multi_launch."""
+    _fields_ = [("kind8", ctypes.c_int32), ("dtype", ctypes.c_int32), ("first", ctypes.c_int32),
+                ("count", ctypes.c_int32), ("tiles", ctypes.c_int64)]
+
+
+MULTI_MAX_LAUNCHES = 64
+
+
+class MultiPlanC(ctypes.Structure):
+    """Mirror of bitopt_multi_plan."""
+    _fields_ = [("optimizer", ctypes.c_int32), ("blocksize", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("nlaunch", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("launch", MultiLaunch * MULTI_MAX_LAUNCHES)]
+
+
 _lib = None
 
 
@@ -103,6 +119,9 @@ def lib():
             "bitopt_host_state_free": ([P], ctypes.c_int),
             "bitopt_step_8bit_tensorwise": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P, P], ctypes.c_int),
             "bitopt_step_multi": ([HP, i32, ctypes.POINTER(Tensor), i32, P, P, P, i64, P], ctypes.c_int),
+            "bitopt_multi_plan_build": ([HP, ctypes.POINTER(Tensor), i32, P, i64, ctypes.POINTER(MultiPlanC), P],
+                                        ctypes.c_int),
+            "bitopt_step_multi_planned": ([ctypes.POINTER(MultiPlanC), HP, i32, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -303,11 +322,9 @@ def multi_workspace_bytes(count: int) -> int:
     return lib().bitopt_multi_workspace_bytes(int(count))
 
 
-def step_multi(hp, step, tensors, qmap1=None, qmap2=None, workspace=None, stream=None):
-    """One step over many tensors.  `tensors`: list of dicts with keys p, g, state1,
-    state2, absmax1, absmax2 (torch tensors or None) and is_8bit (bool).  Returns the
-    workspace tensor used (pass it back to reuse it)."""
-    h = make_hparams(hp)
+def _tensor_array(h, tensors):
+    """bitopt_tensor descriptors of a list of dicts (keys p, g, state1, state2,
+    absmax1, absmax2, is_8bit), with their shapes and dtypes checked."""
     two = h.optimizer in (OPTIMIZERS["adam"], OPTIMIZERS["ademamix"])
     k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
     arr = (Tensor * max(1, len(tensors)))()
@@ -332,6 +349,39 @@ def step_multi(hp, step, tensors, qmap1=None, qmap2=None, workspace=None, stream
                         t["absmax2"].data_ptr() if (eight and two) else None,
                         n, _dt(p), 1 if eight else 0)
         dev = p.device
+    return arr, dev
+
+
+class MultiPlan:
+    """A built multi-tensor plan (bitopt_multi_plan_build): the host struct, its device
+    workspace, and references to the tensors it names (kept alive with it)."""
+
+    def __init__(self, hp, tensors, workspace=None, stream=None):
+        h = make_hparams(hp)
+        arr, dev = _tensor_array(h, tensors)
+        need = multi_workspace_bytes(len(tensors))
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.c = MultiPlanC()
+        self.workspace = workspace
+        self.tensors = list(tensors)
+        _check(lib().bitopt_multi_plan_build(ctypes.byref(h), arr, len(tensors), _ptr(workspace),
+                                             workspace.numel(), ctypes.byref(self.c), _stream(stream)))
+
+    def step(self, hp, step, qmap1=None, qmap2=None, stream=None):
+        h = make_hparams(hp)
+        _check(lib().bitopt_step_multi_planned(ctypes.byref(self.c), ctypes.byref(h), int(step), _ptr(qmap1),
+                                               _ptr(qmap2), _stream(stream)))
+
+
+def step_multi(hp, step, tensors, qmap1=None, qmap2=None, workspace=None, stream=None):
+    """One step over many tensors (plan and step in one call; it waits for the
+    descriptor copy -- a training loop builds a MultiPlan once instead).  `tensors`:
+    list of dicts with keys p, g, state1, state2, absmax1, absmax2 (torch tensors or
+    None) and is_8bit (bool).  Returns the workspace tensor used (pass it back to
+    reuse it)."""
+    h = make_hparams(hp)
+    arr, dev = _tensor_array(h, tensors)
     need = multi_workspace_bytes(len(tensors))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

@@ -320,10 +320,15 @@ int bitopt_host_state_free(void* ptr) {
 
 int64_t bitopt_tensorwise_workspace_bytes(void) { return (int64_t)bitopt::tensorwise_workspace_words() * 4; }
 
-int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype,
-                                int64_t n, uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
-                                const float* qmap1, const float* qmap2, void* workspace, void* stream) {
-    const char* fn = "bitopt_step_8bit_tensorwise";
+}  // extern "C"
+
+namespace {
+
+// Checks and launches of the tensor-wide step; ws: its workspace (device, 4-byte
+// aligned, at least tensorwise_workspace_words() words).
+int run_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype, int64_t n,
+                   uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2, const float* qmap1,
+                   const float* qmap2, void* workspace, void* stream, const char* fn) {
     if (!hp) return fail(BITOPT_ERR_INVALID_ARG, "%s: hp is NULL", fn);
     if (hp->blocksize != 0)
         return fail(BITOPT_ERR_INVALID_ARG, "%s: blocksize must be 0 (one block for the tensor), got %d", fn,
@@ -334,8 +339,10 @@ int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p,
     if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
     if (n == 0) return ok();
-    if (!p || !g || !state1 || !absmax1 || !qmap1 || !workspace || (two && (!state2 || !absmax2 || !qmap2)))
+    if (!p || !g || !state1 || !absmax1 || !qmap1 || !workspace ||
+        (two && (!state2 || !absmax2 || !qmap2)))
         return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
     if (!aligned(workspace, 4)) return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace not 4-byte aligned", fn);
     bitopt::StepArgs a{};
     a.p = p; a.g = g; a.s1 = state1; a.s2 = two ? state2 : nullptr; a.a1 = absmax1; a.a2 = two ? absmax2 : nullptr;
@@ -344,15 +351,133 @@ int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p,
     a.nb = 1;
     a.s = make_scalars(h, step);
     a.vec = vec_ok(&h, p, g, dtype, n, state1, two ? state2 : nullptr) ? 1 : 0;
-    a.ws = static_cast<uint32_t*>(workspace);
+    a.ws = ws;
     hipError_t e = bitopt::launch_tensorwise(a, hp->optimizer, dtype, hp->skip_zeros != 0,
                                              reinterpret_cast<hipStream_t>(stream));
     return device_status(e, fn);
 }
 
+}  // namespace
+
+extern "C" {
+
+int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype,
+                                int64_t n, uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
+                                const float* qmap1, const float* qmap2, void* workspace, void* stream) {
+    return run_tensorwise(hp, step, p, g, dtype, n, state1, state2, absmax1, absmax2, qmap1, qmap2, workspace,
+                          stream, "bitopt_step_8bit_tensorwise");
+}
+
 int64_t bitopt_multi_workspace_bytes(int32_t count) {
     if (count < 0) return -1;
     return (int64_t)count * (int64_t)sizeof(bitopt::TensorDesc);
+}
+
+int bitopt_multi_plan_build(const bitopt_hparams* hp, const bitopt_tensor* tensors, int32_t count,
+                            void* workspace, int64_t workspace_bytes, bitopt_multi_plan* plan, void* stream) {
+    const char* fn = "bitopt_multi_plan_build";
+    if (!plan) return fail(BITOPT_ERR_INVALID_ARG, "%s: plan is NULL", fn);
+    std::memset(plan, 0, sizeof *plan);
+    if (int rc = check_hparams(hp, 1, 0, fn)) return rc;
+    if (count < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: count < 0", fn);
+    if (count > 0 && !tensors) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensors is NULL", fn);
+    const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
+    for (int32_t i = 0; i < count; ++i) {
+        const bitopt_tensor& t = tensors[i];
+        if (t.n < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: n < 0", fn, i);
+        if (!valid_dtype(t.dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: unknown dtype %d", fn, i, t.dtype);
+        if (t.n == 0) continue;
+        if (!t.p || !t.g || !t.state1 || (two && !t.state2))
+            return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: NULL pointer", fn, i);
+        if (t.is_8bit && (!t.absmax1 || (two && !t.absmax2)))
+            return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: NULL absmax", fn, i);
+    }
+    if (count > 0 && (!workspace || workspace_bytes < bitopt_multi_workspace_bytes(count) || !aligned(workspace, 16)))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace missing, too small or not 16-byte aligned", fn);
+
+    // Group by kind (is_8bit, dtype), keeping call order inside a group; chunks of
+    // at most kMaxTableTensors tensors and kMaxLaunchTiles tiles form one launch each.
+    const int64_t te = tile_elems(hp->blocksize);
+    std::vector<bitopt::TensorDesc> table;
+    table.reserve((size_t)count);
+    bitopt_multi_plan P{};
+    P.optimizer = hp->optimizer;
+    P.blocksize = hp->blocksize;
+    P.workspace = workspace;
+    auto push = [&](const bitopt_multi_launch& L) -> bool {
+        if (P.nlaunch == BITOPT_MULTI_MAX_LAUNCHES) return false;
+        P.launch[P.nlaunch++] = L;
+        return true;
+    };
+    for (int kind8 = 1; kind8 >= 0; --kind8) {
+        for (int dt = BITOPT_F32; dt <= BITOPT_BF16; ++dt) {
+            bitopt_multi_launch L{kind8, dt, (int32_t)table.size(), 0, 0};
+            for (int32_t i = 0; i < count; ++i) {
+                const bitopt_tensor& t = tensors[i];
+                if (t.n == 0 || (t.is_8bit != 0) != (kind8 != 0) || t.dtype != dt) continue;
+                const int64_t tiles_t = (t.n + te - 1) / te;
+                if (tiles_t > bitopt::kMaxLaunchTiles)
+                    return fail(BITOPT_ERR_UNSUPPORTED, "%s: tensor %d: more than 2^32 - 1 tiles", fn, i);
+                if (L.count == bitopt::kMaxTableTensors || L.tiles + tiles_t > bitopt::kMaxLaunchTiles) {
+                    if (!push(L)) return fail(BITOPT_ERR_UNSUPPORTED, "%s: more than %d launches", fn, BITOPT_MULTI_MAX_LAUNCHES);
+                    L = bitopt_multi_launch{kind8, dt, (int32_t)table.size(), 0, 0};
+                }
+                bitopt::TensorDesc d{};
+                d.p = t.p; d.g = t.g; d.s1 = t.state1; d.s2 = two ? t.state2 : nullptr;
+                d.a1 = kind8 ? t.absmax1 : nullptr; d.a2 = (kind8 && two) ? t.absmax2 : nullptr;
+                d.n = t.n; d.nb = (t.n + hp->blocksize - 1) / hp->blocksize;
+                d.tile0 = L.tiles;
+                d.vec = vec_ok(hp, t.p, t.g, t.dtype, t.n, t.state1, two ? t.state2 : nullptr) ? 1 : 0;
+                L.tiles += tiles_t;
+                ++L.count;
+                table.push_back(d);
+            }
+            if (L.count && !push(L)) return fail(BITOPT_ERR_UNSUPPORTED, "%s: more than %d launches", fn, BITOPT_MULTI_MAX_LAUNCHES);
+        }
+    }
+    P.count = (int32_t)table.size();
+    if (!table.empty()) {
+        // The table is copied once, here; the host vector must outlive the copy, so the
+        // call waits for the stream (planning is not part of a step).
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        hipError_t e = hipMemcpyAsync(workspace, table.data(), table.size() * sizeof(bitopt::TensorDesc),
+                                      hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return device_status(e, fn);
+    }
+    *plan = P;
+    return ok();
+}
+
+int bitopt_step_multi_planned(const bitopt_multi_plan* plan, const bitopt_hparams* hp, int32_t step,
+                              const float* qmap1, const float* qmap2, void* stream) {
+    const char* fn = "bitopt_step_multi_planned";
+    if (!plan) return fail(BITOPT_ERR_INVALID_ARG, "%s: plan is NULL", fn);
+    if (int rc = check_hparams(hp, step, 0, fn)) return rc;
+    if (hp->optimizer != plan->optimizer || hp->blocksize != plan->blocksize)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: the plan was built for optimizer %d, blocksize %d", fn,
+                    plan->optimizer, plan->blocksize);
+    if (plan->nlaunch < 0 || plan->nlaunch > BITOPT_MULTI_MAX_LAUNCHES || (plan->nlaunch > 0 && !plan->workspace))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: not a plan made by bitopt_multi_plan_build", fn);
+    const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
+    bool any8 = false;
+    for (int32_t i = 0; i < plan->nlaunch; ++i) any8 = any8 || plan->launch[i].kind8;
+    if (any8 && (!qmap1 || (two && !qmap2))) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL qmap", fn);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bitopt::StepScalars sc = make_scalars(*hp, step);
+    for (int32_t i = 0; i < plan->nlaunch; ++i) {
+        const bitopt_multi_launch& L = plan->launch[i];
+        bitopt::StepArgs a{};
+        a.q1 = qmap1; a.q2 = qmap2; a.s = sc;
+        a.table = reinterpret_cast<const bitopt::TensorDesc*>(plan->workspace) + L.first;
+        a.ntab = L.count;
+        a.total_tiles = L.tiles;
+        a.n = 0; a.nb = 0; a.vec = 0;
+        hipError_t e = dispatch_step(a, hp->optimizer, L.dtype, hp->blocksize, L.kind8 != 0, hp->skip_zeros != 0,
+                                     hp->max_unorm > 0.0f, s);
+        if (e != hipSuccess) return device_status(e, fn);
+    }
+    return ok();
 }
 
 int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tensor* tensors, int32_t count,
@@ -365,72 +490,11 @@ int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tenso
     if (!tensors) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensors is NULL", fn);
     const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
     bool any8 = false;
-    for (int32_t i = 0; i < count; ++i) {
-        const bitopt_tensor& t = tensors[i];
-        if (t.n < 0) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: n < 0", fn, i);
-        if (!valid_dtype(t.dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: unknown dtype %d", fn, i, t.dtype);
-        if (t.n == 0) continue;
-        if (!t.p || !t.g || !t.state1 || (two && !t.state2))
-            return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: NULL pointer", fn, i);
-        if (t.is_8bit && (!t.absmax1 || (two && !t.absmax2)))
-            return fail(BITOPT_ERR_INVALID_ARG, "%s: tensor %d: NULL absmax", fn, i);
-        any8 = any8 || t.is_8bit;
-    }
+    for (int32_t i = 0; i < count; ++i) any8 = any8 || (tensors[i].is_8bit && tensors[i].n > 0);
     if (any8 && (!qmap1 || (two && !qmap2))) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL qmap", fn);
-    if (!workspace || workspace_bytes < bitopt_multi_workspace_bytes(count) || !aligned(workspace, 16))
-        return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace missing, too small or not 16-byte aligned", fn);
-
-    // Group by kind (is_8bit, dtype), keeping call order inside a group; chunks of
-    // at most kMaxTableTensors tensors and kMaxLaunchTiles tiles form one launch each.
-    const int64_t te = tile_elems(hp->blocksize);
-    struct Launch { int kind8, dtype; size_t first, count; int64_t tiles; };
-    std::vector<bitopt::TensorDesc> table;
-    std::vector<Launch> launches;
-    table.reserve((size_t)count);
-    for (int kind8 = 1; kind8 >= 0; --kind8) {
-        for (int dt = BITOPT_F32; dt <= BITOPT_BF16; ++dt) {
-            Launch L{kind8, dt, table.size(), 0, 0};
-            for (int32_t i = 0; i < count; ++i) {
-                const bitopt_tensor& t = tensors[i];
-                if (t.n == 0 || (t.is_8bit != 0) != (kind8 != 0) || t.dtype != dt) continue;
-                const int64_t tiles_t = (t.n + te - 1) / te;
-                if (tiles_t > bitopt::kMaxLaunchTiles)
-                    return fail(BITOPT_ERR_UNSUPPORTED, "%s: tensor %d: more than 2^32 - 1 tiles", fn, i);
-                if (L.count == (size_t)bitopt::kMaxTableTensors || L.tiles + tiles_t > bitopt::kMaxLaunchTiles) {
-                    launches.push_back(L);
-                    L = Launch{kind8, dt, table.size(), 0, 0};
-                }
-                bitopt::TensorDesc d{};
-                d.p = t.p; d.g = t.g; d.s1 = t.state1; d.s2 = two ? t.state2 : nullptr;
-                d.a1 = kind8 ? t.absmax1 : nullptr; d.a2 = (kind8 && two) ? t.absmax2 : nullptr;
-                d.n = t.n; d.nb = (t.n + hp->blocksize - 1) / hp->blocksize;
-                d.tile0 = L.tiles;
-                d.vec = vec_ok(hp, t.p, t.g, t.dtype, t.n, t.state1, two ? t.state2 : nullptr) ? 1 : 0;
-                L.tiles += tiles_t;
-                ++L.count;
-                table.push_back(d);
-            }
-            if (L.count) launches.push_back(L);
-        }
-    }
-    if (table.empty()) return ok();
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(workspace, table.data(), table.size() * sizeof(bitopt::TensorDesc),
-                                  hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return device_status(e, fn);
-    const bitopt::StepScalars sc = make_scalars(*hp, step);
-    for (const Launch& L : launches) {
-        bitopt::StepArgs a{};
-        a.q1 = qmap1; a.q2 = qmap2; a.s = sc;
-        a.table = reinterpret_cast<const bitopt::TensorDesc*>(workspace) + L.first;
-        a.ntab = (int32_t)L.count;
-        a.total_tiles = L.tiles;
-        a.n = 0; a.nb = 0; a.vec = 0;
-        e = dispatch_step(a, hp->optimizer, L.dtype, hp->blocksize, L.kind8 != 0, hp->skip_zeros != 0,
-                          hp->max_unorm > 0.0f, s);
-        if (e != hipSuccess) return device_status(e, fn);
-    }
-    return ok();
+    bitopt_multi_plan plan;
+    if (int rc = bitopt_multi_plan_build(hp, tensors, count, workspace, workspace_bytes, &plan, stream)) return rc;
+    return bitopt_step_multi_planned(&plan, hp, step, qmap1, qmap2, stream);
 }
 
 }  // extern "C"

@@ -137,6 +137,17 @@ long verify(const float* Q, const float* tau, const uint8_t* table, const float*
     }
     const float special[] = {0.0f, -0.0f, 1.0f, -1.0f, 0x1p-30f, 0x1p-31f, 0x1p-126f, 0x1p-149f, 1.0000001f};
     for (float x : special) check(x);
+    // NaN (any sign, any quiet payload) encodes as +0 does
+    const int want_nan = brute_nearest(Q, 0.0f);
+    const uint32_t nans[] = {0x7fc00000u, 0xffc00000u, 0x7fc00001u, 0x7fffffffu, 0xffffffffu, 0xffd00000u};
+    for (uint32_t u : nans)
+        for (int nn = 0; nn < 2; ++nn) {
+            ++tested;
+            if (table_code(table, tau_s, u2f(u), nn == 1) != want_nan) {
+                std::fprintf(stderr, "gen_tables: NaN %08x nonneg=%d does not encode as +0\n", u, nn);
+                ++bad;
+            }
+        }
     if (tested == 0) return 1;
     return bad;
 }
@@ -177,6 +188,16 @@ int main(int argc, char** argv) {
                 return 1;
             }
             table[k] = (uint8_t)c0;
+        }
+        // Keys above the top finite key (normalized magnitudes in [1 + 2^-7, 2), which
+        // no finite block reaches: |y| <= 1 + 2^-23) are reached only by NaN, whose
+        // exponent field is all ones and whose quiet bit sets the top mantissa bit.
+        // They get the code of +0 (the encoding of a NaN value), and the threshold
+        // comparison that follows is false for NaN.
+        const int zero_code = brute_nearest(Q, 0.0f);
+        for (int key = kNBH - (1 << kM) + 1; key < kNBH; ++key) {
+            table[kNBH + key] = (uint8_t)zero_code;
+            table[kNBH - 1 - key] = (uint8_t)zero_code;
         }
         const long bad = verify(Q, tau, table, tau_s, s == 0);
         if (bad) {

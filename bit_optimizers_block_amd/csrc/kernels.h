@@ -243,8 +243,10 @@ __device__ __forceinline__ int row_max_nonneg(int v) {
 // ---------------------------------------------------------------- codebook search
 
 // Nearest entry of a sorted 256-entry map Q (in LDS) to x: the largest i in
-// [0, 254] with Q[i] <= x (or 0), then i+1 if it is strictly closer in fp32.
+// [0, 254] with Q[i] <= x (or 0), then i+1 if it is strictly closer in fp32.  A NaN
+// value (from a non-finite state) is encoded as +0 is, as the table encoder does.
 __device__ __forceinline__ uint32_t nearest_code(const float* Q, float x) {
+    x = (x == x) ? x : 0.0f;
     int pos = 0;
 #pragma unroll
     for (int s = 128; s >= 1; s >>= 1) pos = (Q[pos + s] <= x) ? pos + s : pos;

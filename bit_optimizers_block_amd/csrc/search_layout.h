@@ -7,7 +7,8 @@
 // so those 12 bits name the binade and the sub-binade exactly; smaller magnitudes
 // have exponent field 0 (keys 0 .. 127, all of them below the first threshold), and
 // infinities and NaN alias into the top binade, so the key is always in range and
-// needs no clamp.  Negative values use a mirrored half, which keeps the bucket index
+// needs no clamp.  Finite blocks stay below 1 + 2^-7 there (key 0xF80); keys 0xF81 ..
+// 0xFFF are reached only by (quiet) NaN, and their buckets hold the code of +0.  Negative values use a mirrored half, which keeps the bucket index
 // non-decreasing in y:  idx(y) = kNBH + (key ^ (sign ? ~0 : 0)).  Values known to be
 // non-negative skip the sign term: idx = kNBH + key.
 #pragma once

@@ -3,6 +3,7 @@
 #include "tensorwise.h"
 
 namespace bitopt {
+
 namespace {
 
 template <int DT, int OPT, bool SKIP, bool UNORM>

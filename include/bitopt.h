@@ -19,13 +19,17 @@
  *   - Pointers named as device pointers are caller-owned device memory on the
  *     current HIP device.  The library never allocates, frees or retains caller
  *     memory.  `stream` is a hipStream_t (NULL = the null stream); calls enqueue
- *     work on it and return without waiting.  Launch errors are returned at once;
+ *     work on it and return without waiting (bitopt_multi_plan_build and
+ *     bitopt_step_multi, which copy a descriptor table, wait for it).  Launch errors are returned at once;
  *     faults during execution surface at the caller's next synchronisation.
  *   - n == 0 is a successful no-op.  Arguments are checked before anything is
  *     enqueued: n < 0, a NULL pointer that the call needs, an unknown dtype or
  *     optimizer, a blocksize other than 256 or 2048, step < 1, a beta outside
  *     [0, 1), eps < 0, lr < 0 or max_unorm < 0 give BITOPT_ERR_INVALID_ARG.
  *   - Any alignment is accepted; buffers aligned to 16 bytes take the vector path.
+ *   - Step calls form their per-step scalars on the host when called and pass them
+ *     as kernel arguments: a step captured into a HIP graph replays the step number
+ *     (bias corrections, AdEMAMix schedules) it was captured with.
  *   - Calls are stateless and re-entrant.  Fresh state buffers are zero-filled:
  *     codes 0 and absmax 0 decode to zero.
  *   - Element arithmetic is IEEE fp32 (no contraction to FMA, correctly rounded
@@ -267,26 +271,76 @@ BITOPT_API int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t ste
 BITOPT_API int bitopt_host_state_alloc(int64_t bytes, void** ptr);
 BITOPT_API int bitopt_host_state_free(void* ptr);
 
-/* Bytes of device workspace bitopt_step_multi needs for `count` tensors (< 0 if count < 0). */
+/* Bytes of device workspace a multi-tensor step needs for `count` tensors (< 0 if count < 0). */
 BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
 
 /*
- * One optimizer step over many tensors: the same result, bit for bit, as calling
- * the per-tensor 8-bit or 32-bit entry point (by is_8bit) on each tensor with the
- * same hp and step.  Tensors are grouped by (dtype, is_8bit); each group is one
- * kernel launch over all of its tiles, so hundreds of small tensors cost a few
- * launches.  A device table of the group's tensors is written into `workspace`
- * (device, at least bitopt_multi_workspace_bytes(count) bytes, 16-byte aligned) by
- * an asynchronous copy on `stream`; the host array `tensors` may be reused as soon
- * as the call returns.  Work on one workspace must stay in stream order.  The copy
- * reads host memory owned by the call, so this entry point is not meant for capture
- * into a HIP graph (the per-tensor and tensor-wide steps are: they enqueue kernels
- * only).
- *   tensors   host array of count descriptors (n == 0 entries are skipped)
- *   qmap1/2   device codebooks as for the per-tensor calls (needed when any
- *             tensor is 8-bit; qmap2 for 2-state optimizers)
- * Errors: as the per-tensor calls, checked for every tensor before anything is
- * enqueued; a workspace that is too small or misaligned gives INVALID_ARG.
+ * Multi-tensor steps: one optimizer step over many tensors ("optim_overview": one
+ * optimizer holds every parameter of a model; tensors below min_8bit_size keep
+ * 32-bit states).  Each tensor gets the same result, bit for bit, as the per-tensor
+ * 8-bit or 32-bit entry point (by is_8bit) with the same hp and step.  Tensors are
+ * grouped by (dtype, is_8bit); each group is one kernel launch over all of its
+ * tiles, so hundreds of small tensors cost a few launches.
+ *
+ * A plan holds the grouping on the host and the tensors' device descriptors (80 B
+ * per tensor) in a caller-owned device workspace.  It is built once per set of
+ * tensors (bitopt_multi_plan_build: validates every tensor, writes the workspace,
+ * waits for `stream`) and then stepped any number of times
+ * (bitopt_step_multi_planned: kernel launches only -- it enqueues and returns, and
+ * may be captured into a HIP graph).  The plan stays valid while the workspace and
+ * every tensor buffer it names stay allocated at the same addresses.
+ */
+#define BITOPT_MULTI_MAX_LAUNCHES 64
+typedef struct bitopt_multi_launch {
+    int32_t kind8;      /* 1: 8-bit states, 0: 32-bit states */
+    int32_t dtype;      /* parameter dtype of the group */
+    int32_t first;      /* first descriptor of the launch in the workspace table */
+    int32_t count;      /* descriptors in the launch */
+    int64_t tiles;      /* wave tiles over the launch's tensors */
+} bitopt_multi_launch;
+
+typedef struct bitopt_multi_plan {
+    int32_t optimizer;  /* hp->optimizer and hp->blocksize the plan was built for */
+    int32_t blocksize;
+    int32_t count;      /* descriptors written (tensors with n > 0) */
+    int32_t nlaunch;
+    void* workspace;    /* device descriptor table */
+    bitopt_multi_launch launch[BITOPT_MULTI_MAX_LAUNCHES];
+} bitopt_multi_plan;
+
+/*
+ * Build a plan (host struct `plan`, caller-owned) for `count` tensors (host array;
+ * n == 0 entries are skipped) and write their device descriptors into `workspace`
+ * (device, at least bitopt_multi_workspace_bytes(count) bytes, 16-byte aligned).
+ * Only hp->optimizer and hp->blocksize shape the plan.  The descriptor copy is
+ * enqueued on `stream` and waited for before the call returns, so `tensors` may be
+ * reused at once.  Errors: as the per-tensor calls, checked for every tensor before
+ * anything is enqueued; a small or misaligned workspace gives INVALID_ARG; more than
+ * BITOPT_MULTI_MAX_LAUNCHES launches (beyond ~58000 tensors) gives UNSUPPORTED.
+ */
+BITOPT_API int bitopt_multi_plan_build(const bitopt_hparams* hp, const bitopt_tensor* tensors, int32_t count,
+                                       void* workspace, int64_t workspace_bytes, bitopt_multi_plan* plan,
+                                       void* stream);
+
+/*
+ * One step over the tensors of a plan: one kernel launch per group on `stream`,
+ * nothing else (no copies, no waits).  hp must have the plan's optimizer and
+ * blocksize; the other fields (and step) may change from call to call.
+ *   qmap1/2  device codebooks as for the per-tensor calls (needed when any tensor is
+ *            8-bit; qmap2 for 2-state optimizers)
+ * Graph capture: the per-step scalars (bias corrections, schedules) are formed on
+ * the host from hp and step when the call is made and passed as kernel arguments,
+ * so a captured call replays the step number and hyper-parameters it was captured
+ * with; capture one graph per step value, or call eagerly.  (The same holds for every
+ * step entry point.)
+ */
+BITOPT_API int bitopt_step_multi_planned(const bitopt_multi_plan* plan, const bitopt_hparams* hp, int32_t step,
+                                         const float* qmap1, const float* qmap2, void* stream);
+
+/*
+ * Plan and step in one call: bitopt_multi_plan_build followed by
+ * bitopt_step_multi_planned.  It waits for the stream once (the descriptor copy), so a
+ * training loop builds a plan once and calls bitopt_step_multi_planned per step.
  */
 BITOPT_API int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tensor* tensors,
                                  int32_t count, const float* qmap1, const float* qmap2, void* workspace,

@@ -207,9 +207,14 @@ OREF_EXPORT int oref_dynamic_map(int is_signed, float* out)
 /* ------------------------------------------------------------------------- */
 
 /* The plain definition of "nearest codebook entry": the index j minimising the
- * fp32 distance |x - Q[j]|; on an exact tie the smaller index wins. */
+ * fp32 distance |x - Q[j]|; on an exact tie the smaller index wins.  The pages say
+ * nothing about non-finite data; the reading here: a NaN value (it arises only
+ * from a NaN state, or from an infinite state in a block whose absmax is then
+ * infinite and whose reciprocal is 0) has no nearest entry and is encoded as +0
+ * is, so a poisoned element decodes to zero instead of an arbitrary code. */
 static int nearest_code(const float* Q, float x)
 {
+    if (x != x) x = 0.0f;
     int best = 0;
     float bd = fabsf(x - Q[0]);
     for (int j = 1; j < 256; j++) {
@@ -224,7 +229,8 @@ OREF_EXPORT void oref_nearest(const float* Q, const float* x, int64_t n, uint8_t
     for (int64_t i = 0; i < n; i++) out[i] = (uint8_t)nearest_code(Q, x[i]);
 }
 
-/* Encode one block of fp32 values: absmax A = max |s| (exact), one correctly
+/* Encode one block of fp32 values: absmax A = max |s| over the values that are
+ * not NaN (exact; 0 when there are none -- a NaN never becomes the scale), one correctly
  * rounded reciprocal r = 1/A per block (r = 0 when A = 0), then the nearest code
  * of s*r.  A subnormal A can have a reciprocal beyond the fp32 range; such a block
  * is first scaled by 2^24 (exact): r = 1/(A*2^24) and the values (s*2^24)*r.

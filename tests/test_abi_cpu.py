@@ -187,3 +187,34 @@ def test_host_state_argument_errors(B):
     assert L.bitopt_host_state_alloc(0, ctypes.byref(out)) == B.ERR_INVALID_ARG
     assert L.bitopt_host_state_alloc(16, None) == B.ERR_INVALID_ARG
     assert L.bitopt_host_state_free(None) == B.OK
+
+
+def test_multi_plan_argument_errors(B):
+    """The plan calls on their argument-checking paths (no device work): every check of
+    the per-tensor descriptors, the workspace, and a planned step with a different
+    optimizer or blocksize than its plan."""
+    L = B.lib()
+    E = B.ERR_INVALID_ARG
+    h = B.make_hparams(dict(optimizer="adam"))
+    P = ctypes.c_void_p(16)
+    plan = B.MultiPlanC()
+    arr = (B.Tensor * 2)()
+    assert L.bitopt_multi_plan_build(ctypes.byref(h), arr, 0, P, 0, ctypes.byref(plan), None) == B.OK
+    assert plan.nlaunch == 0 and plan.count == 0
+    assert L.bitopt_multi_plan_build(ctypes.byref(h), arr, 0, P, 0, None, None) == E
+    assert L.bitopt_multi_plan_build(ctypes.byref(h), arr, -1, P, 0, ctypes.byref(plan), None) == E
+    arr[0] = B.Tensor(16, 16, 16, None, 16, 16, 100, 0, 1)                   # no state2
+    assert L.bitopt_multi_plan_build(ctypes.byref(h), arr, 1, P, 1000, ctypes.byref(plan), None) == E
+    arr[0] = B.Tensor(16, 16, 16, 16, 16, 16, 100, 0, 1)
+    assert L.bitopt_multi_plan_build(ctypes.byref(h), arr, 1, P, 40, ctypes.byref(plan), None) == E
+    assert "workspace" in B.last_error()
+    # an empty plan steps as a no-op; a plan of another optimizer / blocksize is refused
+    empty = B.MultiPlanC()
+    assert L.bitopt_multi_plan_build(ctypes.byref(h), arr, 0, P, 0, ctypes.byref(empty), None) == B.OK
+    assert L.bitopt_step_multi_planned(ctypes.byref(empty), ctypes.byref(h), 1, None, None, None) == B.OK
+    h2 = B.make_hparams(dict(optimizer="momentum"))
+    assert L.bitopt_step_multi_planned(ctypes.byref(empty), ctypes.byref(h2), 1, None, None, None) == E
+    h3 = B.make_hparams(dict(optimizer="adam", blocksize=2048))
+    assert L.bitopt_step_multi_planned(ctypes.byref(empty), ctypes.byref(h3), 1, None, None, None) == E
+    assert L.bitopt_step_multi_planned(ctypes.byref(empty), ctypes.byref(h), 0, None, None, None) == E   # step 0
+    assert L.bitopt_step_multi_planned(None, ctypes.byref(h), 1, None, None, None) == E

@@ -72,3 +72,54 @@ def test_captured_step_replays_like_eager(mode):
         torch.cuda.synchronize()
         assert torch.isfinite(scratch)
         _compare(A, B, f"replay {r}")
+
+
+def test_captured_multi_plan_step_replays_like_eager():
+    """The planned multi-tensor step enqueues kernels only, so it can be captured: one
+    graph per step number (the per-step scalars are captured with the launch), replayed
+    in order t = 1, 2, 3 and again, each replay equal to the eager planned step at the
+    same t on a twin set of tensors."""
+    hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01, blocksize=256)
+    specs = [(5000, "f32", True), (4096, "bf16", True), (3000, "f16", True), (2048, "f32", False), (77, "bf16", False)]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    q1, q2 = bitopt.create_dynamic_map(True).cuda(), bitopt.create_dynamic_map(False).cuda()
+
+    def make():
+        ts = []
+        for i, (n, dt, eight) in enumerate(specs):
+            nb = (n + 255) // 256
+            sd = torch.uint8 if eight else torch.float32
+            ts.append(dict(p=to_dev(W.to_dtype(W.normal_f32([1900, 1, i], n, 0.02), dt), dt),
+                           g=to_dev(W.to_dtype(W.normal_f32([1900, 2, i], n, 0.01), dt), dt),
+                           state1=torch.zeros(n, dtype=sd, device="cuda"), state2=torch.zeros(n, dtype=sd, device="cuda"),
+                           absmax1=torch.zeros(nb, device="cuda") if eight else None,
+                           absmax2=torch.zeros(nb, device="cuda") if eight else None, is_8bit=eight))
+        return ts
+
+    A, B = make(), make()
+    pa, pb = bitopt.MultiPlan(hp, A), bitopt.MultiPlan(hp, B)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up on a scratch copy, as torch.cuda.graph expects
+        C = make()
+        bitopt.MultiPlan(hp, C).step(hp, 1, q1, q2)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = {}
+    for t in (1, 2, 3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            pa.step(hp, t, q1, q2)
+        graphs[t] = g
+    torch.cuda.synchronize()
+    for rnd in range(2):
+        for t in (1, 2, 3):
+            graphs[t].replay()
+            pb.step(hp, t, q1, q2)
+            scratch = torch.randn(1 << 18, device="cuda").sum()
+            torch.cuda.synchronize()
+            assert torch.isfinite(scratch)
+            for ta, tb in zip(A, B):
+                for key in ("p", "state1", "state2", "absmax1", "absmax2"):
+                    if ta[key] is not None:
+                        np.testing.assert_array_equal(to_host(ta[key]), to_host(tb[key]), err_msg=f"round {rnd} t {t} {key}")

@@ -252,11 +252,13 @@ def test_deterministic():
 
 # ------------------------------------------------------------------ 32-bit mode
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("unorm", [0.0, 0.002])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("name", list(OPTS))
-def test_step_32bit(name, dtype):
+def test_step_32bit(name, dtype, unorm):
     n = RAGGED[256]
-    hp = dict(OPTS[name], blocksize=256, skip_zeros=(name == "lion"))
+    hp = dict(OPTS[name], blocksize=256, skip_zeros=(name == "lion"), max_unorm=unorm)
+    print(f"\n[case] 32-bit {name} {dtype} max_unorm={unorm}", flush=True)
     two = oracle.NUM_STATES[name] >= 2
     k1 = 2 if name == "ademamix" else 1
     p0 = W.to_dtype(W.normal_f32([800, 1], n, 0.02), dtype)
@@ -304,6 +306,92 @@ def test_codec(dtype, bs):
                                                  "bf16": torch.bfloat16}[dtype])
         ref = oracle.dequantize_blockwise(codes_ref, absmax_ref, qmap, bs, dtype)
         np.testing.assert_array_equal(to_host(out, dtype), ref)
+
+
+@pytest.mark.parametrize("bs", [256, 2048])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_codec_custom_maps(dtype, bs):
+    """Maps that are not the standard ones: the codec's binary-search encoder, on full
+    tiles, a ragged tail and an all-zero block, signed and unsigned."""
+    for signed, seed in ((True, 41), (False, 42)):
+        n = RAGGED[bs]
+        print(f"\n[case] codec custom map signed={signed} {dtype} B={bs} n={n}", flush=True)
+        x = W.normal_f32([905, bs, int(signed)], n, 0.01)
+        if not signed:
+            x = np.abs(x)
+        x[bs: 2 * bs] = 0.0
+        x = W.to_dtype(x, dtype)
+        qmap = _jittered_map(signed, seed)
+        codes_ref, absmax_ref = oracle.quantize_blockwise(x, dtype, qmap, bs)
+        qd = torch.from_numpy(qmap).cuda()
+        codes, absmax = bitopt.quantize_blockwise(to_dev(x, dtype), qd, bs)
+        cmp = Compare()
+        cmp.codes(to_host(codes), codes_ref, "codes")
+        cmp.values(to_host(absmax), absmax_ref, 1e-6, "absmax", kind="a")
+        assert cmp.bit_exact, cmp.summary()
+        out = bitopt.dequantize_blockwise(to_dev(codes_ref), to_dev(absmax_ref), qd, bs,
+                                          dtype={"f32": torch.float32, "bf16": torch.bfloat16}[dtype])
+        np.testing.assert_array_equal(to_host(out, dtype), oracle.dequantize_blockwise(codes_ref, absmax_ref, qmap,
+                                                                                       bs, dtype))
+
+
+# ------------------------------------------------------------------ non-finite inputs
+# Reading (the pages are silent): a block's absmax ignores NaN values; a NaN normalized
+# value (a NaN state, or an infinite state in a block whose absmax is then infinite)
+# encodes as +0.  Both sides follow it; these cases assert the documented result.
+
+def _nonfinite_grad(seed, t, n, dtype, B=256):
+    g = W.normal_f32([seed, 2, t], n, 0.01)
+    if t <= 2:
+        nb = (n + B - 1) // B
+        g[3] = np.nan                                   # first block
+        g[B + 17] = -np.nan
+        g[2 * B + 5] = np.inf                           # an infinite gradient element
+        g[3 * B + 200] = -np.inf
+        g[(nb - 1) * B + 1] = np.nan                    # the ragged last block
+        g[4 * B: 4 * B + 40] = np.nan                   # a run of NaN inside a block
+    return W.to_dtype(g, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(OPTS))
+def test_step_8bit_nonfinite_gradients(name, dtype):
+    n, B = RAGGED[256], 256
+    for extra in (dict(), dict(skip_zeros=True, max_unorm=0.002)):
+        hp = dict(OPTS[name], blocksize=B, **extra)
+        print(f"\n[case] non-finite gradients {name} {dtype} {extra}", flush=True)
+        p0 = W.to_dtype(W.normal_f32([990, 1], n, 0.02), dtype)
+        q = Quant8(hp, p0, dtype)
+        cmp = Compare()
+        for t in range(1, 5):
+            g = _nonfinite_grad(990, t, n, dtype, B)
+            q.step_gpu(t, to_dev(g, dtype))
+            q.step_oracle(t, g)
+            q.compare(cmp, f"step {t}")
+        # the rule's visible results: a NaN state never becomes a block absmax; the step
+        # of a NaN gradient is NaN (Lion takes sign(NaN) = 0 and keeps its parameters finite)
+        assert not np.any(np.isnan(to_host(q.d["a1"]))), "a NaN state became a block absmax"
+        assert np.any(np.isnan(as_f32(to_host(q.d["p"], dtype), dtype))) == (name != "lion")
+        print("  " + cmp.summary(), flush=True)
+
+
+@pytest.mark.parametrize("bs", [256, 2048])
+def test_codec_nonfinite_inputs(bs):
+    n = RAGGED[bs]
+    x = W.normal_f32([995, bs], n, 0.01)
+    x[[1, bs + 3, n - 1]] = np.nan
+    x[2 * bs + 7] = np.inf
+    x[3 * bs + 9] = -np.inf
+    for signed in (True, False):
+        xs = x if signed else np.abs(x)
+        qmap = oracle.dynamic_map(signed)
+        codes_ref, absmax_ref = oracle.quantize_blockwise(xs, "f32", qmap, bs)
+        codes, absmax = bitopt.quantize_blockwise(to_dev(xs, "f32"), bitopt.create_dynamic_map(signed).cuda(), bs)
+        cmp = Compare()
+        cmp.codes(to_host(codes), codes_ref, "codes")
+        cmp.values(to_host(absmax), absmax_ref, 1e-6, "absmax", kind="a")
+        assert cmp.bit_exact, cmp.summary()
+        assert not np.any(np.isnan(to_host(absmax)))
 
 
 @pytest.mark.parametrize("bs", [256, 2048])

@@ -167,3 +167,91 @@ def test_bf16_rounding_matches_torch(oref):
     np.testing.assert_array_equal(got, ref)
     np.testing.assert_array_equal(oref.widen(got, "bf16"),
                                   torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+# ------------------------------------------------------------------ non-finite values
+# The pages say nothing about NaN or infinite data.  Reading (used by the oracle and the
+# kernels alike): the block absmax is the largest magnitude among the values that are
+# not NaN (0 if there is none), and a NaN normalized value -- from a NaN state, or from
+# an infinite state whose block absmax is infinite (reciprocal 0, and inf * 0 = NaN) --
+# is encoded as +0 is.  The pins below restate that rule with numpy (nanmax, a brute
+# force argmin over the map) on blocks with NaN and +-inf next to ordinary values.
+
+def _brute_codes(q, x):
+    x = np.asarray(x, np.float32)
+    xx = np.where(np.isnan(x), np.float32(0.0), x)
+    d = np.abs(xx[:, None] - q[None, :])               # fp32 distances
+    return np.argmin(d, axis=1).astype(np.uint8)       # argmin: first (lowest) index on ties
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_quantize_nan_values_ignored_by_absmax_and_encode_as_zero(oref, signed):
+    q = oref.dynamic_map(signed)
+    rng = np.random.default_rng(31)
+    B = 256
+    x = rng.standard_normal(3 * B + 17).astype(np.float32) * np.float32(0.01)
+    if not signed:
+        x = np.abs(x)
+    x[[3, 100, B + 5, 2 * B + 1]] = np.nan
+    x[B + 6] = -np.nan
+    x[2 * B + 2: 3 * B] = np.nan                        # a block that is almost all NaN
+    x[3 * B:] = np.nan                                  # a ragged tail that is all NaN
+    codes, absmax = oref.quantize_blockwise(x, "f32", q, B)
+    for b in range(4):
+        blk = x[b * B:(b + 1) * B]
+        fin = blk[~np.isnan(blk)]
+        A = np.float32(np.abs(fin).max()) if fin.size else np.float32(0.0)
+        assert absmax[b] == A, b
+        r = np.float32(1.0) / A if A > 0 else np.float32(0.0)
+        want = _brute_codes(q, (blk * r).astype(np.float32))
+        np.testing.assert_array_equal(codes[b * B:(b + 1) * B], want, err_msg=f"block {b}")
+    zero_code = int(np.flatnonzero(q == 0.0)[0])
+    assert np.all(codes[np.isnan(x)] == zero_code)
+
+
+def test_quantize_infinite_value_makes_a_zero_block(oref):
+    q = oref.dynamic_map(True)
+    x = np.linspace(-0.5, 0.5, 512).astype(np.float32)
+    x[7] = np.inf
+    x[300] = -np.inf
+    codes, absmax = oref.quantize_blockwise(x, "f32", q, 256)
+    assert np.isinf(absmax[0]) and np.isinf(absmax[1])
+    zero_code = int(np.flatnonzero(q == 0.0)[0])
+    np.testing.assert_array_equal(codes, np.full(512, zero_code, np.uint8))
+    # decoding such a block gives 0 * inf = NaN everywhere: the state is poisoned
+    out = oref.dequantize_blockwise(codes, absmax, q, 256)
+    assert np.all(np.isnan(out))
+
+
+def test_step_with_nan_gradient_poisons_only_its_parameter(oref):
+    """An 8-bit Adam step with a NaN gradient element: that parameter becomes NaN, its
+    states encode as zero, the block absmax stays finite, and every other parameter is
+    bit-identical to the step on the same data with that element's gradient set to 0
+    and skip_zeros on (which leaves the element out of the update entirely) -- except
+    through the block's new absmax, which the NaN element does not enter either way."""
+    n, B = 2 * 256, 256
+    rng = np.random.default_rng(5)
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(n) * 0.01).astype(np.float32)
+    qs, qu = oref.dynamic_map(True), oref.dynamic_map(False)
+    hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.0, blocksize=B)
+    st = lambda: (np.zeros(n, np.uint8), np.zeros(2, np.float32), np.zeros(n, np.uint8), np.zeros(2, np.float32))
+    gn = g.copy()
+    gn[40] = np.nan
+    p1 = p0.copy()
+    s1, a1, s2, a2 = st()
+    oref.step_8bit(hp, 1, p1, gn, "f32", s1, a1, qs, s2, a2, qu)
+    assert np.isnan(p1[40])
+    assert np.all(np.isfinite(a1)) and np.all(np.isfinite(a2))
+    assert s1[40] == int(np.flatnonzero(qs == 0.0)[0]) and s2[40] == int(np.flatnonzero(qu == 0.0)[0])
+    gz = g.copy()
+    gz[40] = 0.0
+    p2 = p0.copy()
+    t1, b1, t2, b2 = st()
+    oref.step_8bit(dict(hp, skip_zeros=True), 1, p2, gz, "f32", t1, b1, qs, t2, b2, qu)
+    keep = np.arange(n) != 40
+    np.testing.assert_array_equal(p1[keep], p2[keep])
+    np.testing.assert_array_equal(a1, b1)
+    np.testing.assert_array_equal(a2, b2)
+    np.testing.assert_array_equal(s1[keep], t1[keep])
+    np.testing.assert_array_equal(s2[keep], t2[keep])

@@ -396,8 +396,12 @@ def test_8bit_tracks_32bit_with_resync(oref, name, dtype):
         _step8(oref, hp, t, p8, g, dtype, st)
         a = ref.p.detach().numpy()
         b = oref.widen(p8, dtype) if dtype != "f32" else p8
+        # the names' reading (rtol = prtol, atol = patol) and the page's positional one
+        # (its helper is called with patol, prtol in the rtol, atol slots) must both hold
         not_close = ~np.isclose(a, b, rtol=pt["prtol"], atol=pt["patol"])
         assert not_close.sum() <= pt["max_error_count"], (t, not_close.sum())
+        not_close_pos = ~np.isclose(a, b, rtol=pt["patol"], atol=pt["prtol"])
+        assert not_close_pos.sum() <= pt["max_error_count"], (t, not_close_pos.sum())
         # decoded 8-bit states against the 32-bit comparator's states
         deq = []
         for k, rs in enumerate(ref.states()):

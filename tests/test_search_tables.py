@@ -97,3 +97,17 @@ def test_table_encoder_special_inputs_stay_in_range():
     x = np.array([np.inf, -np.inf], np.float32)
     np.testing.assert_array_equal(table_encode(t, x, nonneg=False), [255, 0])
     table_encode(t, np.array([np.nan, 3.0, -7.5e30, 1e38], np.float32), nonneg=False)   # in range (asserted)
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_table_encoder_nan_encodes_as_zero(signed):
+    """A NaN value (any sign, any quiet payload) takes the code the oracle gives it:
+    the code of +0 (the non-finite reading of the nearest-code rule)."""
+    t = _tables()[0 if signed else 1]
+    Q = oracle.dynamic_map(signed)
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7FC00001, 0x7FFFFFFF, 0xFFFFFFFF, 0xFFD00000, 0x7FE12345],
+                    np.uint32).view(np.float32)
+    want = oracle.nearest(Q, nans)
+    np.testing.assert_array_equal(want, oracle.nearest(Q, np.zeros(nans.size, np.float32)))
+    for nonneg in (False, True):
+        np.testing.assert_array_equal(table_encode(t, nans, nonneg=nonneg), want)
