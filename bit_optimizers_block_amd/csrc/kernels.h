@@ -285,6 +285,40 @@ __device__ __forceinline__ uint32_t encode(const MapLDS& m, float x) {
     }
 }
 
+// The table encoder on the four values of a quad, packed into one code word (value i
+// in byte i).  The four bucket reads are issued together, then the four threshold
+// reads, so the wave waits for LDS twice per quad rather than twice per element.
+#ifndef BITOPT_ENCODE_GROUPS
+#define BITOPT_ENCODE_GROUPS 1
+#endif
+template <bool NONNEG>
+__device__ __forceinline__ uint32_t encode_quad(const MapLDS& m, const float (&y)[4]) {
+    using namespace search;
+    uint32_t c[4];
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t bits = __float_as_uint(y[i]);
+        const uint32_t key = (bits >> 16) & (uint32_t)(kNBH - 1);
+        const uint32_t idx = (uint32_t)kNBH + (NONNEG ? key : (key ^ (uint32_t)((int32_t)bits >> 31)));
+        c[i] = m.bkt[idx];
+    }
+    if constexpr (BITOPT_ENCODE_GROUPS) {
+        __builtin_amdgcn_sched_group_barrier(0x002, NONNEG ? 4 : 12, 0);   // bucket indices
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                  // bucket reads
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = m.tau[c[i]];
+    if constexpr (BITOPT_ENCODE_GROUPS) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                  // threshold addresses
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                  // threshold reads
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x |= (c[i] + (y[i] >= t[i] ? 1u : 0u)) << (8 * i);
+    return x;
+}
+
 // The table encoder's scale, folded into a block's reciprocal r: r * 2^-kShift.  It
 // gives the scaled value exactly when r >= 2^(kShift - 126) or r == 0; a block with a
 // smaller reciprocal (absmax above 2^30) takes the binary search instead.
@@ -573,22 +607,28 @@ __device__ __forceinline__ void block_absmax_lanes(const float (&m)[BPT], float&
         u = wave_max_nonneg(m[0]);
     } else {
         static_assert(BPT == 4, "tiles hold one or four blocks");
-        const int lane = threadIdx.x & 63;
-        const bool hi = lane >= 32;
-        const bool odd = (lane >> 4) & 1;
+        // gfx950 lane swaps: permlane32 exchanges the upper half of its first operand
+        // with the lower half of its second, so after one swap and a max, lanes 0-31
+        // hold block 0 (1) over both halves and lanes 32-63 block 2 (3); permlane16
+        // then exchanges the odd rows of the first operand with the even rows of the
+        // second, and a max leaves row r with the partial of block r over four lanes.
         int mi[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) mi[b] = __float_as_int(m[b]);
-        // lanes 0-31 keep blocks 0,1 and lanes 32-63 blocks 2,3
-        const int s0 = hi ? mi[0] : mi[2], s1 = hi ? mi[1] : mi[3];
-        const int k0 = hi ? mi[2] : mi[0], k1 = hi ? mi[3] : mi[1];
-        const int w0 = max(k0, __shfl_xor(s0, 32, 64));
-        const int w1 = max(k1, __shfl_xor(s1, 32, 64));
-        // even rows keep the first of the pair, odd rows the second: row r -> block r
-        const int sx = odd ? w0 : w1, kx = odd ? w1 : w0;
-        u = __int_as_float(row_max_nonneg(max(kx, __shfl_xor(sx, 16, 64))));
+        const auto s02 = __builtin_amdgcn_permlane32_swap(mi[0], mi[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(mi[1], mi[3], false, false);
+        const int w02 = max((int)s02[0], (int)s02[1]);
+        const int w13 = max((int)s13[0], (int)s13[1]);
+        const auto r = __builtin_amdgcn_permlane16_swap(w02, w13, false, false);
+        u = __int_as_float(row_max_nonneg(max((int)r[0], (int)r[1])));
     }
     block_recip(u, ru, cu);
+}
+
+// Whether the table encoder's scaled reciprocal r * 2^-kShift is exact: r >= 2^-30 or
+// r == 0, on the bit pattern of a non-negative r (0 wraps to the top).
+__device__ __forceinline__ bool recip_ok_bits(float r) {
+    return __float_as_uint(r) - 1u >= __float_as_uint(0x1p-30f) - 1u;
 }
 
 // Block b's value of a pair left in lanes by block_absmax_lanes (wave-uniform).
@@ -596,20 +636,6 @@ template <int BPT>
 __device__ __forceinline__ float block_value(float v, int b) {
     if constexpr (BPT == 1) return v;
     else return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (64 / BPT) * b));
-}
-
-// The same as uniform per-block values.
-template <int BPT>
-__device__ __forceinline__ void block_absmax(const float (&m)[BPT], float (&A)[BPT], float (&r)[BPT],
-                                             float (&c)[BPT]) {
-    float u, ru, cu;
-    block_absmax_lanes<BPT>(m, u, ru, cu);
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-        A[b] = block_value<BPT>(u, b);
-        r[b] = block_value<BPT>(ru, b);
-        c[b] = block_value<BPT>(cu, b);
-    }
 }
 
 template <bool FULL>
@@ -623,18 +649,20 @@ __device__ __forceinline__ void store_code_word(uint8_t* cp, int64_t e, int64_t 
     }
 }
 
-// Encode the lane's values of one tile: per-block absmax (A, uniform), nearest
-// codes of value * (1/A).  Quads of blocks past the end hold zeros.  The table
-// encoder serves every tile whose blocks have an absmax of at most 2^30 (a subnormal
-// absmax with its 2^24 prescale: its scaled reciprocal stays normal); a larger
-// absmax, or a map without tables, takes the binary search -- one element at a time,
-// so that this path, which practical data never reaches, does not raise the kernel's
-// register count.
+// Encode the lane's values of one tile: per-block absmax, nearest codes of value *
+// (1/absmax).  The new absmax is left in lanes (Al): with one block per tile in every
+// lane, with four blocks in row b for block b.  Quads of blocks past the end hold
+// zeros.  The table encoder serves every tile whose blocks have an absmax of at most
+// 2^30 (a subnormal absmax with its 2^24 prescale: its scaled reciprocal stays
+// normal); a larger absmax, or a map without tables, takes the binary search -- one
+// element at a time, so that this path, which practical data never reaches, does not
+// raise the kernel's register count.  The decisions are taken once per tile on the
+// lanes' values (two ballots), and each quad reads its block's scaled reciprocal
+// from the lane that holds it.
 template <int BS, bool FAST, bool NONNEG, int NQ>
-__device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ][4], uint32_t w[NQ],
-                                            float (&A)[Layout<BS>::BPT]) {
+__device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ][4], uint32_t w[NQ], float& Al) {
     using L = Layout<BS>;
-    float m[L::BPT], r[L::BPT], c[L::BPT];
+    float m[L::BPT];
 #pragma unroll
     for (int b = 0; b < L::BPT; ++b) {
         float x = 0.0f;
@@ -644,34 +672,30 @@ __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ
             for (int i = 0; i < 4; ++i) x = fmaxf(x, fabsf(v[b * L::QPB + qq][i]));
         m[b] = x;
     }
-    block_absmax<L::BPT>(m, A, r, c);
-    bool table = FAST, scaled = false;              // uniform
+    float u, ru, cu;
+    block_absmax_lanes<L::BPT>(m, u, ru, cu);
+    Al = u;
+    const bool table = FAST && !wave_any(!recip_ok_bits(ru));       // uniform
+    const bool scaled = wave_any(cu != 1.0f);
+    if (table) {
+        const float rs = ru * kEncScale;
+        auto tables = [&](auto prescale) {
 #pragma unroll
-    for (int b = 0; b < L::BPT; ++b) {
-        table = table && table_recip_ok(r[b]);
-        scaled = scaled || c[b] != 1.0f;
-    }
-    auto tables = [&](auto prescale) {
+            for (int q = 0; q < NQ; ++q) {
+                const float rq = block_value<L::BPT>(rs, q / L::QPB);
+                const float cq = decltype(prescale)::value ? block_value<L::BPT>(cu, q / L::QPB) : 1.0f;
+                float y[4];
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const float rq = r[q / L::QPB] * kEncScale, cq = c[q / L::QPB];
-            uint32_t x = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float y = decltype(prescale)::value ? (v[q][i] * cq) * rq : v[q][i] * rq;
-                x |= encode<true, NONNEG>(M, y) << (8 * i);
+                for (int i = 0; i < 4; ++i) y[i] = decltype(prescale)::value ? (v[q][i] * cq) * rq : v[q][i] * rq;
+                w[q] = encode_quad<NONNEG>(M, y);
             }
-            w[q] = x;
-        }
-    };
-    if (table && !scaled) {
-        tables(std::false_type{});
-    } else if (table) {
-        tables(std::true_type{});
+        };
+        if (!scaled) tables(std::false_type{});
+        else tables(std::true_type{});
     } else {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const float rq = r[q / L::QPB], cq = c[q / L::QPB];
+            const float rq = block_value<L::BPT>(ru, q / L::QPB), cq = block_value<L::BPT>(cu, q / L::QPB);
             uint32_t x = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -680,6 +704,18 @@ __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ
             }
             w[q] = x;
         }
+    }
+}
+
+// Store the new absmax of the tile's blocks from the lanes that hold them (see
+// encode_tile); wmask: bit b set when block b is written (uniform).
+template <int BPT>
+__device__ __forceinline__ void store_absmax(float* am, int64_t blk0, int lane, float Al, uint32_t wmask) {
+    if constexpr (BPT == 1) {
+        if ((wmask & 1u) && lane == 0) gbl(am)[blk0] = Al;
+    } else {
+        const int b = lane >> 4;
+        if ((lane & 15) == 0 && ((wmask >> b) & 1u)) gbl(am)[blk0 + b] = Al;
     }
 }
 
@@ -987,16 +1023,17 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
         const int64_t eo = Slot<OPT>::elem_off(k, n);
         if constexpr (QUANT) {
             uint32_t w[NQ];
-            float A[BPT];
+            float Al;
             if (k == RootState<OPT>::v && HasRoot<OPT>::v)      // a second moment: never negative
-                encode_tile<BS, FAST, true>(slot ? M2 : M1, st[k], w, A);
+                encode_tile<BS, FAST, true>(slot ? M2 : M1, st[k], w, Al);
             else
-                encode_tile<BS, FAST, false>(slot ? M2 : M1, st[k], w, A);
+                encode_tile<BS, FAST, false>(slot ? M2 : M1, st[k], w, Al);
             float* am = (slot ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
             uint8_t* cp = reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + eo;
+            uint32_t wmask = 0;
 #pragma unroll
-            for (int b = 0; b < BPT; ++b)
-                if (write[b] && lane == 0) gbl(am)[blk0 + b] = A[b];
+            for (int b = 0; b < BPT; ++b) wmask |= write[b] ? 1u << b : 0u;
+            store_absmax<BPT>(am, blk0, lane, Al, wmask);
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
                 if (write[q / QPB]) store_code_word<true>(cp, L::elem(base, lane, q), n, w[q]);
@@ -1452,11 +1489,12 @@ __device__ __forceinline__ void quant_tile(const CodecArgs& a, const MapLDS& M, 
         }
     }
     uint32_t w[NQ];
-    float A[L::BPT];
-    encode_tile<BS, FAST, false>(M, v, w, A);
+    float Al;
+    encode_tile<BS, FAST, false>(M, v, w, Al);
+    uint32_t wmask = 0;
 #pragma unroll
-    for (int b = 0; b < L::BPT; ++b)
-        if ((FULL || blk0 + b < a.nb) && lane == 0) gbl(a.absmax)[blk0 + b] = A[b];
+    for (int b = 0; b < L::BPT; ++b) wmask |= (FULL || blk0 + b < a.nb) ? 1u << b : 0u;
+    store_absmax<L::BPT>(a.absmax, blk0, lane, Al, wmask);
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
         if (FULL || blk0 + q / L::QPB < a.nb) store_code_word<FULL>(a.codes, L::elem(base, lane, q), n, w[q]);
