@@ -118,6 +118,8 @@ def lib():
             "bitopt_host_state_alloc": ([i64, ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
             "bitopt_host_state_free": ([P], ctypes.c_int),
             "bitopt_step_8bit_tensorwise": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P, P], ctypes.c_int),
+            "bitopt_step_8bit_tensorwise_noalloc": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P], ctypes.c_int),
+            "bitopt_tensorwise_scratch_bytes": ([], i64),
             "bitopt_step_multi": ([HP, i32, ctypes.POINTER(Tensor), i32, P, P, P, i64, P], ctypes.c_int),
             "bitopt_multi_plan_build": ([HP, ctypes.POINTER(Tensor), i32, P, i64, ctypes.POINTER(MultiPlanC), P],
                                         ctypes.c_int),
@@ -316,6 +318,25 @@ def step_8bit_tensorwise(hp, step, p, g, state1, absmax1, qmap1, state2=None, ab
                                              _ptr(state1), _ptr(state2), _ptr(absmax1), _ptr(absmax2),
                                              _ptr(qmap1), _ptr(qmap2), _ptr(workspace), _stream(stream)))
     return workspace
+
+
+def step_8bit_tensorwise_noalloc(hp, step, p, g, state1, absmax1, qmap1, state2=None, absmax2=None, qmap2=None,
+                                 stream=None):
+    """The tensor-wide step with the library's own scratch array as its workspace
+    (no device allocation by the call; calls that overlap on one GPU race)."""
+    h = make_hparams(hp)
+    n = p.numel()
+    k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
+    two = h.optimizer in (OPTIMIZERS["adam"], OPTIMIZERS["ademamix"])
+    _need(p, "p"); _need(g, "g", p.dtype, n)
+    _need(state1, "state1", torch.uint8, k * n, device="state"); _need(absmax1, "absmax1", torch.float32, k, device="state")
+    _need(qmap1, "qmap1", torch.float32, 256)
+    if two:
+        _need(state2, "state2", torch.uint8, n, device="state"); _need(absmax2, "absmax2", torch.float32, 1, device="state")
+        _need(qmap2, "qmap2", torch.float32, 256)
+    _check(lib().bitopt_step_8bit_tensorwise_noalloc(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
+                                                     _ptr(state1), _ptr(state2), _ptr(absmax1), _ptr(absmax2),
+                                                     _ptr(qmap1), _ptr(qmap2), _stream(stream)))
 
 
 def multi_workspace_bytes(count: int) -> int:

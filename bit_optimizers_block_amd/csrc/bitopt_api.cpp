@@ -325,10 +325,11 @@ int64_t bitopt_tensorwise_workspace_bytes(void) { return (int64_t)bitopt::tensor
 namespace {
 
 // Checks and launches of the tensor-wide step; ws: its workspace (device, 4-byte
-// aligned, at least tensorwise_workspace_words() words).
+// aligned, at least tensorwise_workspace_words() words), or NULL for the library's
+// own scratch array.
 int run_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype, int64_t n,
                    uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2, const float* qmap1,
-                   const float* qmap2, void* workspace, void* stream, const char* fn) {
+                   const float* qmap2, void* workspace, bool own_scratch, void* stream, const char* fn) {
     if (!hp) return fail(BITOPT_ERR_INVALID_ARG, "%s: hp is NULL", fn);
     if (hp->blocksize != 0)
         return fail(BITOPT_ERR_INVALID_ARG, "%s: blocksize must be 0 (one block for the tensor), got %d", fn,
@@ -339,11 +340,19 @@ int run_tensorwise(const bitopt_hparams* hp, int32_t step, void* p, const void* 
     if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
     if (n == 0) return ok();
-    if (!p || !g || !state1 || !absmax1 || !qmap1 || !workspace ||
+    if (!p || !g || !state1 || !absmax1 || !qmap1 || (!own_scratch && !workspace) ||
         (two && (!state2 || !absmax2 || !qmap2)))
         return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     uint32_t* ws = static_cast<uint32_t*>(workspace);
-    if (!aligned(workspace, 4)) return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace not 4-byte aligned", fn);
+    if (own_scratch) {
+        if (bitopt::tensorwise_workspace_words() > bitopt::tensorwise_scratch_words())
+            return fail(BITOPT_ERR_UNSUPPORTED, "%s: the step needs %d workspace words, the scratch array holds %d",
+                        fn, bitopt::tensorwise_workspace_words(), bitopt::tensorwise_scratch_words());
+        hipError_t e = bitopt::tensorwise_scratch(&ws);
+        if (e != hipSuccess) return device_status(e, fn);
+    } else if (!aligned(workspace, 4)) {
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: workspace not 4-byte aligned", fn);
+    }
     bitopt::StepArgs a{};
     a.p = p; a.g = g; a.s1 = state1; a.s2 = two ? state2 : nullptr; a.a1 = absmax1; a.a2 = two ? absmax2 : nullptr;
     a.q1 = qmap1; a.q2 = two ? qmap2 : qmap1;
@@ -365,8 +374,18 @@ int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t step, void* p,
                                 int64_t n, uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
                                 const float* qmap1, const float* qmap2, void* workspace, void* stream) {
     return run_tensorwise(hp, step, p, g, dtype, n, state1, state2, absmax1, absmax2, qmap1, qmap2, workspace,
-                          stream, "bitopt_step_8bit_tensorwise");
+                          false, stream, "bitopt_step_8bit_tensorwise");
 }
+
+int bitopt_step_8bit_tensorwise_noalloc(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                        int32_t dtype, int64_t n, uint8_t* state1, uint8_t* state2,
+                                        float* absmax1, float* absmax2, const float* qmap1, const float* qmap2,
+                                        void* stream) {
+    return run_tensorwise(hp, step, p, g, dtype, n, state1, state2, absmax1, absmax2, qmap1, qmap2, nullptr,
+                          true, stream, "bitopt_step_8bit_tensorwise_noalloc");
+}
+
+int64_t bitopt_tensorwise_scratch_bytes(void) { return (int64_t)bitopt::tensorwise_scratch_words() * 4; }
 
 int64_t bitopt_multi_workspace_bytes(int32_t count) {
     if (count < 0) return -1;

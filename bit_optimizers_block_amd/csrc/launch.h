@@ -19,6 +19,10 @@ hipError_t launch_step_adagrad(const StepArgs& a, int dtype, int bs, bool quant,
 // Tensor-wide (non-block-wise) 8-bit step: clear, pass 1 (absmax), pass 2 (apply).
 hipError_t launch_tensorwise(const StepArgs& a, int opt, int dtype, bool skip, hipStream_t s);
 int tensorwise_workspace_words();
+// The library's own tensor-wide workspace on the current device (a device array of
+// tensorwise_scratch_words() words, shared by every call on that device).
+hipError_t tensorwise_scratch(uint32_t** out);
+int tensorwise_scratch_words();
 
 hipError_t launch_quantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_dequantize(const CodecArgs& a, int dtype, int bs, hipStream_t s);

@@ -1,8 +1,38 @@
 // Kernel instantiations and launches of the tensor-wide (non-block-wise) 8-bit step.
+#include <mutex>
+
 #include "launch.h"
 #include "tensorwise.h"
 
 namespace bitopt {
+
+// Workspace of the allocation-free tensor-wide step: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` only names the
+// symbol; its device address is looked up once per device (tensorwise_scratch) and
+// only that address is handed to kernels.
+static __device__ __align__(256) uint32_t scratch[kTwWords];
+
+hipError_t tensorwise_scratch(uint32_t** out) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void* ptrs[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptrs[dev] = p;
+    }
+    *out = static_cast<uint32_t*>(ptrs[dev]);
+    return hipSuccess;
+}
+
+int tensorwise_scratch_words() { return kTwWords; }
 
 namespace {
 

@@ -257,6 +257,25 @@ BITOPT_API int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t ste
                                            const float* qmap2, void* workspace, void* stream);
 
 /*
+ * The tensor-wide step without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments and results are those of bitopt_step_8bit_tensorwise;
+ * its partial results go to the library's own scratch array instead: a file-scope
+ * device array of bitopt_tensorwise_scratch_bytes() bytes (32.8 KB) on each GPU the
+ * library runs on, held until the process ends.  The step needs that much for any n
+ * (pass 1 has at most 1024 groups), so no size exceeds it.  The call allocates nothing
+ * (no hipMalloc, no library allocation); its first call on a device looks the array's
+ * address up.  Every call on one GPU shares that GPU's array: calls that may overlap
+ * on one GPU (other streams, other threads) race and must be ordered by the caller.
+ * Nothing in the array needs to start at zero (each pass writes what it reads).
+ */
+BITOPT_API int bitopt_step_8bit_tensorwise_noalloc(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                                   int32_t dtype, int64_t n, uint8_t* state1, uint8_t* state2,
+                                                   float* absmax1, float* absmax2, const float* qmap1,
+                                                   const float* qmap2, void* stream);
+BITOPT_API int64_t bitopt_tensorwise_scratch_bytes(void);
+
+/*
  * Optimizer state outside HBM ("paged" state: the optimizer overview's is_paged, the
  * Paged*8bit optimizers of the 8-bit PR's optimizer table).  Pinned host memory,
  * mapped into the GPU's address space with the same address, so the state arrays of
@@ -270,6 +289,7 @@ BITOPT_API int bitopt_step_8bit_tensorwise(const bitopt_hparams* hp, int32_t ste
  */
 BITOPT_API int bitopt_host_state_alloc(int64_t bytes, void** ptr);
 BITOPT_API int bitopt_host_state_free(void* ptr);
+
 
 /* Bytes of device workspace a multi-tensor step needs for `count` tensors (< 0 if count < 0). */
 BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
