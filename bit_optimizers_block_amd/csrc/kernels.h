@@ -513,21 +513,22 @@ __device__ __forceinline__ float root_delta_estimate(const StepScalars& s, float
     return s.lr * u;
 }
 
-// Whether a new 16-bit parameter z, formed from an estimated step d, rounds to the
-// same 16-bit value as the one formed from the exact step: true when z - m and z + m
-// round alike, m = |d| 2^-19 + |z| 2^-21 + 2^-120 being at least twice the distance
-// the estimate can move z (13 * 2^-24 |d| + 2 * 2^-24 |z| + 2^-140).  Rounding is
-// monotone, so every value between z - m and z + m -- the exact one included --
-// rounds alike.  The margin is returned through m: a non-finite margin (z or d not
-// finite) makes the test void, which the caller checks once for a quad by summing
-// the margins (the sum is finite only if every margin is).
+// Whether the new 16-bit parameter formed from an estimated step d, z = fl(pd - d),
+// rounds to the same 16-bit value as the one formed from the exact step dx: true when
+// fl(pd - (d + e)) and fl(pd - (d - e)) round alike, e = |d| 2^-19 + 2^-120 being more
+// than twice the distance of d from dx (13 * 2^-24 |d| + 2^-140), so that the rounded
+// sums d + e and d - e still bracket dx.  The correctly rounded subtraction and the
+// 16-bit rounding are both monotone, so fl(pd - dx) -- and z -- lie between the two
+// bounds and round alike.  A non-finite margin (d not finite) makes the test fail.
 template <int DT>
-__device__ __forceinline__ bool rounds_alike(float z, float d, float& m) {
-    m = __builtin_fmaf(__builtin_fabsf(d), 0x1p-19f, __builtin_fmaf(__builtin_fabsf(z), 0x1p-21f, 0x1p-120f));
-    const float lo = z - m;
-    const float hi = z + m;
+__device__ __forceinline__ bool rounds_alike(float pd, float d) {
+    const float e = __builtin_fmaf(__builtin_fabsf(d), 0x1p-19f, 0x1p-120f);
+    const float dhi = d + e;
+    const float dlo = d - e;
+    const float lo = pd - dhi;
+    const float hi = pd - dlo;
     const uint32_t w = narrow2<DT>(lo, hi);
-    return (w & 0xffffu) == (w >> 16);
+    return (w & 0xffffu) == (w >> 16) && e < __builtin_inff();
 }
 
 // One element of one step.  st[] holds the decoded states on entry and the new
@@ -558,10 +559,18 @@ __device__ __forceinline__ void update_elem(const StepScalars& s, float p, float
     }
 }
 
+// The parameter before the step is subtracted: p * (1 - lr*wd) for decoupled decay,
+// p itself where the decay is folded into the gradient.
+template <int OPT>
+__device__ __forceinline__ float decayed(const StepScalars& s, float p) {
+    if constexpr (OPT == kMomentum || OPT == kRmsprop || OPT == kAdagrad) return p;
+    else return p * s.decay;
+}
+
 template <int OPT>
 __device__ __forceinline__ float apply_step(const StepScalars& s, float p, float d) {
-    if constexpr (OPT == kMomentum || OPT == kRmsprop || OPT == kAdagrad) return p - d;   // decay in the gradient
-    else { const float pd = p * s.decay; return pd - d; }
+    const float pd = decayed<OPT>(s, p);
+    return pd - d;
 }
 
 // Location of state k: AdEMAMix keeps m1 and m2 in slot 1 (m2 after n elements /
@@ -933,18 +942,17 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
                 // within the estimate's bound changes its 16-bit rounding; the quad
                 // otherwise recomputes the step exactly (the same bits either way).
                 if (a.s.fast_root && !any_tiny) {
-                    float z[4], mg[4];
+                    float z[4];
                     bool unsure = false;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
                                              NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
                         const float d = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
-                        z[i] = apply_step<OPT>(a.s, pf[q][i], d);
-                        unsure |= !rounds_alike<DT>(z[i], d, mg[i]);
+                        const float pd = decayed<OPT>(a.s, pf[q][i]);
+                        z[i] = pd - d;
+                        unsure |= !rounds_alike<DT>(pd, d);
                     }
-                    const float msum = (mg[0] + mg[1]) + (mg[2] + mg[3]);
-                    unsure |= !(msum < __builtin_inff());
                     if (!wave_any(unsure)) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) pf[q][i] = z[i];
