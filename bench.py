@@ -54,6 +54,7 @@ def workload_by_name(name):
         "adamw_fp32_tensorwise": lambda: W.f3_tensorwise_4096("f32"),
         "adamw_bf16_tensorwise": lambda: W.f3_tensorwise_4096("bf16"),
         "adamw_fp32_b256_paged": lambda: W.f4_paged_4096("f32"),
+        "adamw_fp32_b256_staged": lambda: W.f4_staged_4096("f32"),
         "adam_fp32_256x256": W.c1_adam_256,
         "adam_fp32_1024x9": W.adam_small_1024x9,
         "adamw32_fp32_4096": lambda: W.adamw_32bit_4096("f32"),
@@ -187,6 +188,12 @@ class Replica:
             g.reshape(rows, -1)[mask] = 0.0
         self.p = torch.from_numpy(p).to(dev).to(dt)
         self.g = torch.from_numpy(g).to(dev).to(dt)
+        self.staged = wl.extra.get("paged") == "staged"
+        if self.staged:
+            # state paged through device staging buffers around each step
+            self.staging = torch.empty(bitopt.paged_staging_bytes(hp, wl.extra["chunk"]), dtype=torch.uint8,
+                                       device=dev)
+            self.copy_streams = (torch.cuda.Stream(), torch.cuda.Stream())
         if wl.extra.get("paged"):
             # optimizer state in pinned host memory mapped into the GPU address space
             def z(numel, dt):
@@ -203,6 +210,11 @@ class Replica:
         self.a2 = z(nb, torch.float32) if (self.two and self.eightbit) else None
 
     def step(self, hp, t, q1, q2):
+        if self.staged:
+            bitopt.step_8bit_paged(hp, t, self.p, self.g, self.s1, self.a1, q1, self.s2, self.a2,
+                                   q2 if self.two else None, staging=self.staging, h2d_stream=self.copy_streams[0],
+                                   d2h_stream=self.copy_streams[1])
+            return
         if not self.eightbit:
             if self.two:
                 bitopt.step_32bit_2state(hp, t, self.p, self.g, self.s1, self.s2)
@@ -225,12 +237,17 @@ class Replica:
         ptr = lambda x: ctypes.c_void_p(x.data_ptr())
         dt = bitopt.DTYPES[self.p.dtype]
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        if not self.eightbit:
+        opt = lambda x: None if x is None else ptr(x)
+        if self.staged:
+            f = L.bitopt_step_8bit_paged
+            tail = (ptr(self.s1), opt(self.s2), ptr(self.a1), opt(self.a2), ptr(q1), ptr(q2) if self.two else None,
+                    ptr(self.staging), self.staging.numel(), ctypes.c_void_p(self.copy_streams[0].cuda_stream),
+                    ctypes.c_void_p(self.copy_streams[1].cuda_stream), stream)
+        elif not self.eightbit:
             f = L.bitopt_step_32bit_2state if self.two else L.bitopt_step_32bit_1state
             tail = (ptr(self.s1), ptr(self.s2), stream) if self.two else (ptr(self.s1), stream)
         elif self.tensorwise:
             f = L.bitopt_step_8bit_tensorwise
-            opt = lambda x: None if x is None else ptr(x)
             tail = (ptr(self.s1), opt(self.s2), ptr(self.a1), opt(self.a2), ptr(q1),
                     ptr(q2) if self.two else None, ptr(self.ws), stream)
         elif self.two:
@@ -643,8 +660,10 @@ def main():
                "param_dtype": t.dtype, "blocksize": B, "weight_decay": hp.get("weight_decay", 0.0),
                "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps),
                "arithmetic": "f32", "state_dtype": "u8" if t.eightbit else "f32"}
-        if wl.extra.get("paged"):
-            cfg["state_memory"] = "pinned host (paged)"
+        if wl.extra.get("paged") == "staged":
+            cfg["state_memory"] = f"pinned host, paged through HBM staging in chunks of {wl.extra['chunk']} elements"
+        elif wl.extra.get("paged"):
+            cfg["state_memory"] = "pinned host, read and written in place over the host link"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gelem/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(avg_ms, 5),

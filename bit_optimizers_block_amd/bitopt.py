@@ -120,6 +120,8 @@ def lib():
             "bitopt_step_8bit_tensorwise": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P, P], ctypes.c_int),
             "bitopt_step_8bit_tensorwise_noalloc": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P], ctypes.c_int),
             "bitopt_tensorwise_scratch_bytes": ([], i64),
+            "bitopt_paged_staging_bytes": ([HP, i64], i64),
+            "bitopt_step_8bit_paged": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P, i64, P, P, P], ctypes.c_int),
             "bitopt_step_multi": ([HP, i32, ctypes.POINTER(Tensor), i32, P, P, P, i64, P], ctypes.c_int),
             "bitopt_multi_plan_build": ([HP, ctypes.POINTER(Tensor), i32, P, i64, ctypes.POINTER(MultiPlanC), P],
                                         ctypes.c_int),
@@ -337,6 +339,38 @@ def step_8bit_tensorwise_noalloc(hp, step, p, g, state1, absmax1, qmap1, state2=
     _check(lib().bitopt_step_8bit_tensorwise_noalloc(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
                                                      _ptr(state1), _ptr(state2), _ptr(absmax1), _ptr(absmax2),
                                                      _ptr(qmap1), _ptr(qmap2), _stream(stream)))
+
+
+def paged_staging_bytes(hp, chunk_elems: int) -> int:
+    return lib().bitopt_paged_staging_bytes(ctypes.byref(make_hparams(hp)), int(chunk_elems))
+
+
+def step_8bit_paged(hp, step, p, g, state1, absmax1, qmap1, state2=None, absmax2=None, qmap2=None,
+                    staging=None, h2d_stream=None, d2h_stream=None, stream=None):
+    """8-bit step with the state in host memory (host_state() tensors), paged through
+    a device staging buffer chunk by chunk (bitopt_step_8bit_paged).  h2d_stream and
+    d2h_stream: torch streams distinct from the step stream.  Returns the staging
+    tensor used (pass it back to reuse it)."""
+    h = make_hparams(hp)
+    n = p.numel()
+    k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
+    two = h.optimizer in (OPTIMIZERS["adam"], OPTIMIZERS["ademamix"])
+    nb = nblocks(n, h.blocksize)
+    _need(p, "p"); _need(g, "g", p.dtype, n)
+    for t, name, dt, cnt in ((state1, "state1", torch.uint8, k * n), (absmax1, "absmax1", torch.float32, k * nb)) + (
+            ((state2, "state2", torch.uint8, n), (absmax2, "absmax2", torch.float32, nb)) if two else ()):
+        _need(t, name, dt, cnt, device=False)
+        if t.is_cuda:
+            raise ValueError(f"{name} must be host memory (host_state())")
+    if staging is None:
+        staging = torch.empty(paged_staging_bytes(hp, min(n, 1 << 22)), dtype=torch.uint8, device=p.device)
+    if h2d_stream is None or d2h_stream is None:
+        raise ValueError("step_8bit_paged needs two copy streams")
+    _check(lib().bitopt_step_8bit_paged(ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n, _ptr(state1),
+                                        _ptr(state2), _ptr(absmax1), _ptr(absmax2), _ptr(qmap1), _ptr(qmap2),
+                                        _ptr(staging), staging.numel(), _stream(h2d_stream), _stream(d2h_stream),
+                                        _stream(stream)))
+    return staging
 
 
 def multi_workspace_bytes(count: int) -> int:

@@ -324,6 +324,157 @@ int64_t bitopt_tensorwise_workspace_bytes(void) { return (int64_t)bitopt::tensor
 
 namespace {
 
+// ---------------------------------------------------------------- paged (staged) state
+
+constexpr int64_t kPageQuantum = 4096;     // chunk sizes are multiples of this many elements
+constexpr int64_t kStageAlign = 256;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Layout of one staging buffer for chunks of C elements: the chunk's codes and absmax
+// in the order and shape a step call takes them.
+struct StageLayout {
+    int64_t s1, s2, a1, a2, bytes;   // offsets and total bytes
+};
+
+StageLayout stage_layout(int optimizer, int32_t blocksize, int64_t C) {
+    const bool two = optimizer == BITOPT_ADAM || optimizer == BITOPT_ADEMAMIX;
+    const int64_t k1 = optimizer == BITOPT_ADEMAMIX ? 2 : 1;
+    const int64_t nbc = (C + blocksize - 1) / blocksize;
+    StageLayout L{};
+    int64_t off = 0;
+    L.s1 = off; off = align_up(off + k1 * C, kStageAlign);
+    L.s2 = off; off = two ? align_up(off + C, kStageAlign) : off;
+    L.a1 = off; off = align_up(off + 4 * k1 * nbc, kStageAlign);
+    L.a2 = off; off = two ? align_up(off + 4 * nbc, kStageAlign) : off;
+    L.bytes = off;
+    return L;
+}
+
+// Events of the staged step, per device and per calling thread: one call enqueues
+// all of its work before it returns, and a stream wait binds to the record made
+// before it, so later calls can re-record them.
+struct StageEvents {
+    hipEvent_t start, in[2], comp[2], out[2];
+    bool ready;
+};
+
+hipError_t stage_events(StageEvents** out) {
+    constexpr int kMaxDev = 64;
+    thread_local StageEvents pool[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    StageEvents& E = pool[dev];
+    if (!E.ready) {
+        hipEvent_t* all[7] = {&E.start, &E.in[0], &E.in[1], &E.comp[0], &E.comp[1], &E.out[0], &E.out[1]};
+        for (hipEvent_t* ev : all) {
+            e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        E.ready = true;
+    }
+    *out = &E;
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bitopt_paged_staging_bytes(const bitopt_hparams* hp, int64_t chunk_elems) {
+    if (!hp || chunk_elems < 1 || !valid_blocksize(hp->blocksize) || hp->optimizer < BITOPT_ADAM ||
+        hp->optimizer > BITOPT_ADAGRAD)
+        return -1;
+    return 2 * stage_layout(hp->optimizer, hp->blocksize, align_up(chunk_elems, kPageQuantum)).bytes;
+}
+
+int bitopt_step_8bit_paged(const bitopt_hparams* hp, int32_t step, void* p, const void* g, int32_t dtype,
+                           int64_t n, uint8_t* host_state1, uint8_t* host_state2, float* host_absmax1,
+                           float* host_absmax2, const float* qmap1, const float* qmap2, void* staging,
+                           int64_t staging_bytes, void* h2d_stream, void* d2h_stream, void* stream) {
+    const char* fn = "bitopt_step_8bit_paged";
+    if (int rc = check_hparams(hp, step, n, fn)) return rc;
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
+    if (n == 0) return ok();
+    if (!p || !g || !host_state1 || !host_absmax1 || !qmap1 || !staging ||
+        (two && (!host_state2 || !host_absmax2 || !qmap2)))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(staging, kStageAlign)) return fail(BITOPT_ERR_INVALID_ARG, "%s: staging not 256-byte aligned", fn);
+    if (h2d_stream == d2h_stream || h2d_stream == stream || d2h_stream == stream)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: the two copy streams and the step stream must be distinct", fn);
+    // the largest chunk (a multiple of kPageQuantum elements) whose two buffers fit
+    const int64_t B = hp->blocksize;
+    int64_t C = align_up(n, kPageQuantum);
+    while (C > kPageQuantum && 2 * stage_layout(hp->optimizer, hp->blocksize, C).bytes > staging_bytes)
+        C = std::max(kPageQuantum, (C / 2) / kPageQuantum * kPageQuantum);
+    const StageLayout L = stage_layout(hp->optimizer, hp->blocksize, C);
+    if (2 * L.bytes > staging_bytes)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: staging of %lld bytes is below the minimum %lld", fn,
+                    (long long)staging_bytes, (long long)(2 * L.bytes));
+    StageEvents* E = nullptr;
+    if (hipError_t e = stage_events(&E); e != hipSuccess) return device_status(e, fn);
+    hipStream_t sh = reinterpret_cast<hipStream_t>(h2d_stream), sd = reinterpret_cast<hipStream_t>(d2h_stream),
+                sc = reinterpret_cast<hipStream_t>(stream);
+    const int64_t k1 = hp->optimizer == BITOPT_ADEMAMIX ? 2 : 1;
+    const int64_t nb = (n + B - 1) / B;
+    const int es = elem_size(dtype);
+    uint8_t* base = static_cast<uint8_t*>(staging);
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    // nothing of this call reads the host state before the work already on `stream`
+    // (earlier steps and their write-backs) is complete
+    chk(hipEventRecord(E->start, sc));
+    chk(hipStreamWaitEvent(sh, E->start, 0));
+    const int64_t nchunks = (n + C - 1) / C;
+    for (int64_t i = 0; i < nchunks && e == hipSuccess; ++i) {
+        const int b = (int)(i & 1);
+        const int64_t c0 = i * C, len = std::min(C, n - c0);
+        const int64_t cb0 = c0 / B, nbc = (len + B - 1) / B;
+        uint8_t* buf = base + b * L.bytes;
+        uint8_t* ds1 = buf + L.s1;
+        uint8_t* ds2 = buf + L.s2;
+        float* da1 = reinterpret_cast<float*>(buf + L.a1);
+        float* da2 = reinterpret_cast<float*>(buf + L.a2);
+        if (i >= 2) chk(hipStreamWaitEvent(sh, E->out[b], 0));     // buffer b written back
+        for (int64_t k = 0; k < k1; ++k) {
+            chk(hipMemcpyAsync(ds1 + k * len, host_state1 + k * n + c0, len, hipMemcpyHostToDevice, sh));
+            chk(hipMemcpyAsync(da1 + k * nbc, host_absmax1 + k * nb + cb0, 4 * nbc, hipMemcpyHostToDevice, sh));
+        }
+        if (two) {
+            chk(hipMemcpyAsync(ds2, host_state2 + c0, len, hipMemcpyHostToDevice, sh));
+            chk(hipMemcpyAsync(da2, host_absmax2 + cb0, 4 * nbc, hipMemcpyHostToDevice, sh));
+        }
+        chk(hipEventRecord(E->in[b], sh));
+        chk(hipStreamWaitEvent(sc, E->in[b], 0));
+        if (e != hipSuccess) break;
+        if (int rc = run_step(hp, step, static_cast<uint8_t*>(p) + c0 * es, static_cast<const uint8_t*>(g) + c0 * es,
+                              dtype, len, ds1, two ? ds2 : nullptr, da1, two ? da2 : nullptr, qmap1,
+                              two ? qmap2 : nullptr, true, stream, fn))
+            return rc;
+        chk(hipEventRecord(E->comp[b], sc));
+        chk(hipStreamWaitEvent(sd, E->comp[b], 0));
+        for (int64_t k = 0; k < k1; ++k) {
+            chk(hipMemcpyAsync(host_state1 + k * n + c0, ds1 + k * len, len, hipMemcpyDeviceToHost, sd));
+            chk(hipMemcpyAsync(host_absmax1 + k * nb + cb0, da1 + k * nbc, 4 * nbc, hipMemcpyDeviceToHost, sd));
+        }
+        if (two) {
+            chk(hipMemcpyAsync(host_state2 + c0, ds2, len, hipMemcpyDeviceToHost, sd));
+            chk(hipMemcpyAsync(host_absmax2 + cb0, da2, 4 * nbc, hipMemcpyDeviceToHost, sd));
+        }
+        chk(hipEventRecord(E->out[b], sd));
+    }
+    // the step stream completes only after every write-back (they run in order on d2h)
+    chk(hipStreamWaitEvent(sc, E->out[(nchunks - 1) & 1], 0));
+    return device_status(e, fn);
+}
+
+}  // extern "C"
+
+namespace {
+
 // Checks and launches of the tensor-wide step; ws: its workspace (device, 4-byte
 // aligned, at least tensorwise_workspace_words() words), or NULL for the library's
 // own scratch array.

@@ -194,6 +194,16 @@ def f4_paged_4096(dtype: str = "f32") -> Workload:
     return w
 
 
+def f4_staged_4096(dtype: str = "f32") -> Workload:
+    """The block-wise AdamW workload with the state in pinned host memory, paged through
+    HBM staging buffers chunk by chunk around each step (copy-in, step, write-back
+    overlapped on three streams)."""
+    w = c2_adamw_4096(dtype, 256)
+    w.name = f"adamw8bit_4096x4096_{dtype}_b256_staged"
+    w.extra = {"paged": "staged", "chunk": 1 << 23}
+    return w
+
+
 def adam_small_1024x9() -> Workload:
     """The pages' small benchmark shape (1024 x 9 fp32, Adam 8-bit), where the step
     is launch-bound rather than bandwidth-bound."""

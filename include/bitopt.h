@@ -290,6 +290,35 @@ BITOPT_API int64_t bitopt_tensorwise_scratch_bytes(void);
 BITOPT_API int bitopt_host_state_alloc(int64_t bytes, void** ptr);
 BITOPT_API int bitopt_host_state_free(void* ptr);
 
+/*
+ * Paged state, staged: one 8-bit block-wise step (2-state or 1-state) whose codes and
+ * absmax live in host memory (bitopt_host_state_alloc or other pinned memory; the
+ * optimizer overview's is_paged, the Paged*8bit optimizers of the 8-bit PR).  The
+ * tensor is cut into chunks of whole blocks; for each chunk the state is paged into
+ * one of two HBM staging buffers on `h2d_stream`, stepped on `stream` by the same
+ * kernels as bitopt_step_8bit_blockwise_*, and paged back out on `d2h_stream`, so
+ * the copy-in of the next chunk and the write-back of the previous one overlap the
+ * step of the current one (event ordering, no host waits; the call enqueues and
+ * returns).  Results are bit-identical to the device-resident step.
+ *   host_state1/2, host_absmax1/2  host memory laid out as the device-resident call's
+ *            state1/2, absmax1/2 (state2, absmax2, qmap2: NULL for 1-state optimizers)
+ *   p, g     device, n elements of dtype
+ *   staging  device, 256-byte aligned, staging_bytes long; chunk size = the largest
+ *            multiple of 4096 elements whose two buffers fit (at least
+ *            bitopt_paged_staging_bytes(hp, 4096) bytes); overwritten
+ *   h2d_stream, d2h_stream, stream  three distinct streams.  Work already on
+ *            `stream` completes before the host state is read; `stream` completes
+ *            only after every write-back.  Calls that share staging or copy streams
+ *            must be ordered on `stream`.
+ * Errors: as the per-tensor calls; a staging buffer below the minimum, misaligned, or
+ * streams that are not distinct give INVALID_ARG.
+ */
+BITOPT_API int64_t bitopt_paged_staging_bytes(const bitopt_hparams* hp, int64_t chunk_elems);
+BITOPT_API int bitopt_step_8bit_paged(const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                                      int32_t dtype, int64_t n, uint8_t* host_state1, uint8_t* host_state2,
+                                      float* host_absmax1, float* host_absmax2, const float* qmap1,
+                                      const float* qmap2, void* staging, int64_t staging_bytes,
+                                      void* h2d_stream, void* d2h_stream, void* stream);
 
 /* Bytes of device workspace a multi-tensor step needs for `count` tensors (< 0 if count < 0). */
 BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
