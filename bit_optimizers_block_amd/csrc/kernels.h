@@ -716,6 +716,39 @@ __device__ __forceinline__ void encode_tile(const MapLDS& M, const float (&v)[NQ
     }
 }
 
+// encode_tile for a tile holding one block whose absmax u (uniform) is already known:
+// a wave's half of a 2048-element block, the other half's maximum included.
+template <int BS, bool FAST, bool NONNEG, int NQ>
+__device__ __forceinline__ void encode_tile_given(const MapLDS& M, const float (&v)[NQ][4], uint32_t w[NQ],
+                                                  float u) {
+    static_assert(Layout<BS>::BPT == 1, "one block per tile");
+    float ru, cu;
+    block_recip(u, ru, cu);
+    const bool table = FAST && recip_ok_bits(ru);       // uniform
+    if (table) {
+        const float rs = ru * kEncScale;
+        const bool scaled = cu != 1.0f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = scaled ? (v[q][i] * cu) * rs : v[q][i] * rs;
+            w[q] = encode_quad<NONNEG>(M, y);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            uint32_t x = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x |= encode<false>(M, (v[q][i] * cu) * ru) << (8 * i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            w[q] = x;
+        }
+    }
+}
+
 // Store the new absmax of the tile's blocks from the lanes that hold them (see
 // encode_tile); wmask: bit b set when block b is written (uniform).
 template <int BPT>
@@ -824,12 +857,14 @@ __device__ __forceinline__ void load_params(const StepArgs& a, int64_t base, int
     }
 }
 
-template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool WITHP = true>
+// BSA: the size of the blocks the absmax arrays index -- BS itself, or 2048 when the
+// tile is one wave's half of a 2048-element block (see step_pairs).
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool WITHP = true, int BSA = BS>
 __device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int lane,
                                           TileRaw<DT, OPT, BS, QUANT>& r) {
     using L = Layout<BS>;
     using R = TileRaw<DT, OPT, BS, QUANT>;
-    const int64_t blk0 = base / BS;
+    const int64_t blk0 = base / BSA;
     if constexpr (StateReadsP<OPT>::v) load_params<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
 #pragma unroll
     for (int k = 0; k < R::NS; ++k) {
@@ -860,22 +895,31 @@ __device__ __forceinline__ void load_rest(const StepArgs& a, int64_t base, int l
     if constexpr (!StateReadsP<OPT>::v && WITHP) load_params<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
 }
 
-template <int DT, int OPT, int BS, bool QUANT, bool SKIP>
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, int BSA = BS>
 __device__ __forceinline__ void load_tile(const StepArgs& a, int64_t base, int lane,
                                           TileRaw<DT, OPT, BS, QUANT>& r) {
     load_grad<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
-    load_rest<DT, OPT, BS, QUANT, SKIP>(a, base, lane, r);
+    load_rest<DT, OPT, BS, QUANT, SKIP, true, BSA>(a, base, lane, r);
 }
 
-// Compute and store one full tile from its raw inputs.
-template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool FAST>
+// A wave pair's exchange of its halves' partial block maxima (see step_pairs): slot
+// [iteration parity][wave][state].
+typedef float PairExchange[2][kWavesPerGroup][4];
+
+// Compute and store one full tile from its raw inputs.  PAIRX: the tile is one wave's
+// half of a 2048-element block (BS = 1024, one block per tile); the block's absmax is
+// formed with the partner wave's half through xch (one workgroup barrier) before the
+// states are encoded, and only the first half stores it.
+template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool FAST, bool PAIRX = false>
 __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1, const MapLDS& M2,
-                                             int64_t base, int lane, const TileRaw<DT, OPT, BS, QUANT>& r) {
+                                             int64_t base, int lane, const TileRaw<DT, OPT, BS, QUANT>& r,
+                                             PairExchange* xch = nullptr, int parity = 0) {
     using L = Layout<BS>;
     constexpr int NQ = L::NQ, BPT = L::BPT, QPB = L::QPB;
     constexpr int NS = NumStates<OPT>::v;
+    static_assert(!PAIRX || (BS == 1024 && QUANT && !SKIP && !UNORM), "pair tiles: half of a 2048 block");
     const int64_t n = a.n;
-    const int64_t blk0 = base / BS;
+    const int64_t blk0 = base / (PAIRX ? 2048 : BS);
 
     float pf[NQ][4], st[NS][NQ][4], dl[NQ][4];
     bool live[NQ][4];
@@ -1024,6 +1068,29 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
         }
     }
 
+    // ---- pair tiles: the block absmax over both halves
+    float Apair[NS];
+    if constexpr (PAIRX) {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            float x = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x = fmaxf(x, fabsf(st[k][q][i]));
+            Apair[k] = wave_max_nonneg(x);
+            if (lane == 0) (*xch)[parity][wave][k] = Apair[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const float other = __int_as_float(__builtin_amdgcn_readfirstlane(
+                __float_as_int((*xch)[parity][wave ^ 1][k])));
+            Apair[k] = __int_as_float(max(__float_as_int(Apair[k]), __float_as_int(other)));
+        }
+    }
+
     // ---- states: new absmax and codes (8-bit) or fp32 values
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
@@ -1032,16 +1099,27 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
         if constexpr (QUANT) {
             uint32_t w[NQ];
             float Al;
-            if (k == RootState<OPT>::v && HasRoot<OPT>::v)      // a second moment: never negative
+            if constexpr (PAIRX) {
+                Al = Apair[k];
+                if (k == RootState<OPT>::v && HasRoot<OPT>::v)
+                    encode_tile_given<BS, FAST, true>(slot ? M2 : M1, st[k], w, Al);
+                else
+                    encode_tile_given<BS, FAST, false>(slot ? M2 : M1, st[k], w, Al);
+            } else if (k == RootState<OPT>::v && HasRoot<OPT>::v) {      // a second moment: never negative
                 encode_tile<BS, FAST, true>(slot ? M2 : M1, st[k], w, Al);
-            else
+            } else {
                 encode_tile<BS, FAST, false>(slot ? M2 : M1, st[k], w, Al);
+            }
             float* am = (slot ? a.a2 : a.a1) + Slot<OPT>::block_off(k, a.nb);
             uint8_t* cp = reinterpret_cast<uint8_t*>(slot ? a.s2 : a.s1) + eo;
             uint32_t wmask = 0;
 #pragma unroll
             for (int b = 0; b < BPT; ++b) wmask |= write[b] ? 1u << b : 0u;
-            store_absmax<BPT>(am, blk0, lane, Al, wmask);
+            if constexpr (PAIRX) {
+                if ((threadIdx.x & 64) == 0 && lane == 0) gbl(am)[blk0] = Al;     // the pair's first half
+            } else {
+                store_absmax<BPT>(am, blk0, lane, Al, wmask);
+            }
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
                 if (write[q / QPB]) store_code_word<true>(cp, L::elem(base, lane, q), n, w[q]);
@@ -1349,6 +1427,43 @@ __device__ __forceinline__ void step_tiles(const StepArgs& a0, const MapLDS& M1,
     }
 }
 
+// B = 2048 by wave pairs (single tensor, no skip_zeros or max_unorm): waves 2j and
+// 2j+1 of a group share block b0 + j, each holding four quads of it (the register
+// footprint of a 1024-element tile rather than a 2048-element one, so more waves fit
+// per SIMD).  Each wave computes its half; the halves' maxima meet in LDS across one
+// workgroup barrier per iteration; each wave encodes and stores its own half.  A
+// block that is ragged, or a tensor that is not aligned for the vector path, is
+// taken whole by the pair's first wave on the quad-at-a-time path.  The loop bounds
+// are uniform over the group, so every wave passes the same number of barriers.
+template <int DT, int OPT, bool FAST>
+__device__ __forceinline__ void step_pairs(const StepArgs& a, const MapLDS& M1, const MapLDS& M2,
+                                           PairExchange* xch) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = wave & 1;
+    int parity = 0;
+    for (int64_t b0 = (int64_t)blockIdx.x * 2; b0 < a.nb; b0 += (int64_t)gridDim.x * 2) {
+        const int64_t blk = b0 + (wave >> 1);
+        const bool inb = blk < a.nb;
+        // the same for both waves of the pair; the binary-search encoder (maps other than
+        // the standard ones) always takes the quad-at-a-time path
+        const bool full = FAST && inb && a.vec && (blk + 1) * 2048 <= a.n;
+        if constexpr (FAST) {
+            if (full) {
+                const int64_t base = blk * 2048 + (int64_t)half * 1024;
+                TileRaw<DT, OPT, 1024, true> x;
+                load_tile<DT, OPT, 1024, true, false, 2048>(a, base, lane, x);
+                process_tile<DT, OPT, 1024, true, false, false, true, true>(a, M1, M2, base, lane, x, xch, parity);
+            }
+        }
+        if (!full) {
+            __syncthreads();                      // the barrier of process_tile's exchange
+            if (inb && half == 0) guarded_tile<DT, OPT, 2048, true, false, false, FAST, false>(a, M1, M2, blk * 2048, lane);
+        }
+        parity ^= 1;
+    }
+}
+
 // skip_zeros, one tile per wave (single tensor, grid covering every tile): the
 // gradient is read before the maps are staged, and a group none of whose tiles has
 // a nonzero gradient ends there -- most groups of a sparse update do no more than
@@ -1430,7 +1545,13 @@ __device__ __forceinline__ void step_one_tile(const StepArgs& a, float* Q1, floa
 // allocator's choice.
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM> struct MinWaves {
     static constexpr bool hot16 = DT != kF32 && BS == 256 && QUANT && !SKIP && !UNORM;
-    static constexpr int v = !hot16 ? 1 : OPT == kAdemamix ? 5 : OPT == kAdam ? 6 : (OPT == kMomentum || OPT == kLion) ? 8 : 1;
+    static constexpr bool pair = BS == 2048 && QUANT && !SKIP && !UNORM && OPT == kAdam;
+    static constexpr int v = pair ? 5 : !hot16 ? 1 : OPT == kAdemamix ? 5 : OPT == kAdam ? 6 : (OPT == kMomentum || OPT == kLion) ? 8 : 1;
+};
+
+// Steps whose 2048-element blocks are taken by wave pairs (step_pairs).
+template <int BS, bool QUANT, bool SKIP, bool UNORM, bool MULTI> struct PairBlocks {
+    static constexpr bool v = BS == 2048 && QUANT && !SKIP && !UNORM && !MULTI;
 };
 
 // One launch of the fused step: a single tensor (MULTI false: the launch arguments)
@@ -1445,6 +1566,14 @@ void k_step(StepArgs a) {
     __shared__ uint32_t vote[kWavesPerGroup];
     __shared__ uint32_t T0[MULTI ? kMaxTableTensors : 1];   // first tiles (< 2^32 per launch)
     const MapLDS M1{Q1, T1, B1}, M2{Q2, T2, B2};
+    if constexpr (PairBlocks<BS, QUANT, SKIP, UNORM, MULTI>::v) {
+        __shared__ PairExchange xch[1];
+        if (stage_maps<NMAPS, UnsignedState1<OPT>::v>(a.q1, a.q2, Q1, Q2, T1, T2, B1, B2, vote))
+            step_pairs<DT, OPT, true>(a, M1, M2, xch);
+        else
+            step_pairs<DT, OPT, false>(a, M1, M2, xch);
+        return;
+    }
     if constexpr (MULTI) {
         const BITOPT_CONSTANT TensorDesc* tab = (const BITOPT_CONSTANT TensorDesc*)a.table;
         for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = (uint32_t)tab[i].tile0;

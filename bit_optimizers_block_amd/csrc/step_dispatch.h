@@ -30,6 +30,18 @@ int grid_groups_per_cu() {
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM>
 hipError_t launch_one(const StepArgs& a, hipStream_t s) {
     constexpr int64_t tile = Layout<BS>::TE;
+    if constexpr (PairBlocks<BS, QUANT, SKIP, UNORM, false>::v) {
+        if (!a.table) {
+            // wave pairs: two 2048-element blocks per group and iteration
+            int64_t groups = (a.nb + 1) / 2;
+            const int64_t cap = group_cap(grid_groups_per_cu<DT, OPT, BS, QUANT, SKIP, UNORM, false>());
+            if (groups > cap) groups = cap;
+            if (groups < 1) groups = 1;
+            hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM, false>), dim3((unsigned)groups),
+                               dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (a.table)
         hipLaunchKernelGGL((k_step<DT, OPT, BS, QUANT, SKIP, UNORM, true>),
                            tile_grid(a.total_tiles * tile, tile, grid_groups_per_cu<DT, OPT, BS, QUANT, SKIP, UNORM, true>()),
