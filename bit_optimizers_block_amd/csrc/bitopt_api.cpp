@@ -111,10 +111,9 @@ namespace bitopt {
 // 4-wave groups, i.e. one tile per wave up to 64 M elements (B = 256) on 256 CUs, and
 // a grid stride beyond that, so very large launches stage the LDS codebooks once per
 // group for several tiles rather than once per tile.  Measured on MI355X: one tile
-// per wave streams best for most steps (the hardware refills CUs as groups retire);
-// for the 1.3 G element multi-tensor step 256 per CU ran 2-5% faster than 64, 1024
-// and 4096.  Launches that pass resident_per_cu (see step_dispatch.h) use a grid that
-// is resident at once instead.
+// per wave streams best for most steps (the hardware refills CUs as groups retire).
+// Launches that pass resident_per_cu (see step_dispatch.h) use that many groups per
+// CU instead: a grid resident at once, or the multi-tensor launches' 512.
 int64_t group_cap(int resident_per_cu) {
     constexpr int kMaxDev = 64;
     static std::atomic<int> cus[kMaxDev];

@@ -11,14 +11,20 @@ namespace bitopt {
 // RMSprop, Adagrad) on 16-bit parameters -- the most arithmetic per byte -- run a
 // resident grid: as many groups per CU as fit at once, each wave looping over
 // tiles, so the codebooks and search tables are staged once per group rather than
-// once per four tiles (+2..7% over one tile per wave, A/B on one GPU).  Everything
-// else keeps one tile per wave, which measured faster: fp32 parameters, Momentum and
-// Lion (fewer instructions per byte: -6..9% with a resident grid), the multi-tensor
-// launch (-11%), and skip_zeros launches, whose all-zero groups end early only
-// when the grid covers every tile.
+// once per four tiles (+2..7% over one tile per wave, A/B on one GPU).  Multi-tensor
+// launches use 512 groups per CU (a grid stride of a few tiles per wave).
+// Everything else keeps one tile per wave, which measured faster: fp32 parameters,
+// Momentum and Lion (fewer instructions per byte: -6..9% with a resident grid), and
+// skip_zeros launches, whose all-zero groups end early only when the grid covers
+// every tile.
 template <int DT, int OPT, int BS, bool QUANT, bool SKIP, bool UNORM, bool MULTI>
 int grid_groups_per_cu() {
-    if constexpr (DT == kF32 || !QUANT || SKIP || MULTI || !HasRoot<OPT>::v) {
+    if constexpr (MULTI) {
+        // Multi-tensor launches (hundreds of millions of elements): 512 groups per CU,
+        // i.e. about two and a half tiles per wave for the 1.3 G-parameter set, ran 1%
+        // faster than 256 and 3-5% faster than 1024 or 4096 (one GPU, bf16 Adam).
+        return 512;
+    } else if constexpr (DT == kF32 || !QUANT || SKIP || !HasRoot<OPT>::v) {
         return 0;
     } else {
         static const int n =
