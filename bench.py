@@ -60,6 +60,9 @@ def workload_by_name(name):
         "adamw32_fp32_4096": lambda: W.adamw_32bit_4096("f32"),
         "adamw32_bf16_4096": lambda: W.adamw_32bit_4096("bf16"),
         "gpt_1p3b": W.c5_gpt_1p3b,
+        "quantize_fp32_b256": lambda: W.codec_4096("quantize", "f32"),
+        "dequantize_fp32_b256": lambda: W.codec_4096("dequantize", "f32"),
+        "quantize_bf16_b256": lambda: W.codec_4096("quantize", "bf16"),
     }
     return table[name]()
 
@@ -78,7 +81,13 @@ def tensorwise_bytes_per_element(dtype: str, optimizer: str, max_unorm: float = 
 
 
 def workload_bytes(wl) -> float:
-    """Algorithmic HBM bytes of one step over every tensor of the workload."""
+    """Algorithmic HBM bytes of one step over every tensor of the workload (the codec
+    workloads: values read or written once, codes written or read once, one absmax per
+    block)."""
+    if wl.extra.get("codec"):
+        t = wl.tensors[0]
+        ps = {"f32": 4, "f16": 2, "bf16": 2}[t.dtype]
+        return (ps + 1 + 4.0 / wl.hp["blocksize"]) * t.numel
     ns = NUM_STATES[wl.hp["optimizer"]]
     total = 0.0
     for t in wl.tensors:
@@ -159,6 +168,48 @@ class Model:
 
         def launch(t):
             rc = f(plan, ctypes.byref(h), t, *args)
+            if rc != 0:
+                raise bitopt.BitoptError(rc, bitopt.last_error())
+        return launch
+
+
+class CodecReplica:
+    """Device buffers of one copy of a codec workload: values, codes, absmax."""
+
+    def __init__(self, wl, r, dev):
+        t = wl.tensors[0]
+        self.kind = wl.extra["codec"]
+        self.n = n = t.numel
+        self.B = B = wl.hp["blocksize"]
+        dt = TORCH_DT[t.dtype]
+        self.x = torch.from_numpy(W.normal_f32([wl.seed, 1, 0, r], n, wl.g_scale)).to(dev).to(dt)
+        self.q = bitopt.create_dynamic_map(True).to(dev)
+        self.codes, self.absmax = bitopt.quantize_blockwise(self.x, self.q, B)
+        self.out = torch.empty_like(self.x)
+        self.p = self.x
+        self.eightbit = True
+
+    def step(self, hp, t, q1, q2):
+        if self.kind == "quantize":
+            bitopt.quantize_blockwise(self.x, self.q, self.B, codes=self.codes, absmax=self.absmax)
+        else:
+            bitopt.dequantize_blockwise(self.codes, self.absmax, self.q, self.B, out=self.out)
+
+    def raw_launcher(self, hp, q1, q2):
+        import ctypes
+        L = bitopt.lib()
+        ptr = lambda x: ctypes.c_void_p(x.data_ptr())
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        dt = bitopt.DTYPES[self.x.dtype]
+        if self.kind == "quantize":
+            f, args = L.bitopt_quantize_blockwise, (ptr(self.x), dt, self.n, ptr(self.q), self.B, ptr(self.codes),
+                                                    ptr(self.absmax), stream)
+        else:
+            f, args = L.bitopt_dequantize_blockwise, (ptr(self.codes), ptr(self.absmax), ptr(self.q), self.n, self.B,
+                                                      ptr(self.out), dt, stream)
+
+        def launch(t):
+            rc = f(*args)
             if rc != 0:
                 raise bitopt.BitoptError(rc, bitopt.last_error())
         return launch
@@ -332,6 +383,32 @@ def cpu_baseline(wl, target_s=15.0):
             "sample": f"{what} of the same workload, {steps} step(s), {dt:.1f} s on {threads} threads"}
 
 
+def cpu_baseline_codec(wl, target_s=15.0):
+    """The oracle's codec on the same values: repeated whole-tensor passes for about
+    target_s seconds."""
+    import oracle
+    t = wl.tensors[0]
+    B = wl.hp["blocksize"]
+    x = W.to_dtype(W.normal_f32([wl.seed, 1, 0, 0], t.numel, wl.g_scale), t.dtype)
+    q = oracle.dynamic_map(True)
+    codes, absmax = oracle.quantize_blockwise(x, t.dtype, q, B)
+    run = (lambda: oracle.quantize_blockwise(x, t.dtype, q, B)) if wl.extra["codec"] == "quantize" else \
+        (lambda: oracle.dequantize_blockwise(codes, absmax, q, B, t.dtype))
+    t0 = time.perf_counter()
+    run()
+    one = time.perf_counter() - t0
+    reps = max(1, int(target_s / max(one, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    dt = time.perf_counter() - t0
+    threads = oracle.get_threads()
+    return {"value": t.numel * reps / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"the whole tensor, {reps} pass(es), {dt:.1f} s on {threads} threads "
+                      f"({'OpenMP over blocks' if wl.extra['codec'] == 'quantize' else 'one thread: a plain loop'})"}
+
+
 def cpu_baseline_multi(wl, target_s=15.0):
     import oracle
     hp = wl.hp
@@ -413,13 +490,22 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
 
 
-def _rocprof(args, outdir, extra, env=None):
+def _rocprof(args, outdir, extra, env=None, result=None):
+    """Run the benchmark under rocprofv3; its JSON line goes to result["bench"] when
+    a dict is given."""
     cmd = ["rocprofv3", *extra, "--output-format", "csv", "-d", outdir, "-o", "run", "--",
            sys.executable, os.path.abspath(__file__), *args]
     print("+ " + " ".join(cmd), flush=True)
-    r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=300)
+    r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=300, stdout=subprocess.PIPE, text=True)
+    sys.stdout.write(r.stdout)
+    sys.stdout.flush()
     if r.returncode != 0:
         raise SystemExit(f"rocprofv3 failed ({r.returncode}): {' '.join(cmd)}")
+    if result is not None:
+        for line in reversed(r.stdout.strip().splitlines()):
+            if line.startswith("{"):
+                result["bench"] = json.loads(line)
+                break
     # as recorded: the repository root as <repo>, the interpreter as python
     shown = ["python" if c == sys.executable else c.replace(ROOT, "<repo>") for c in cmd]
     return " ".join(shown)
@@ -440,7 +526,7 @@ def kernel_is_8bit(kname: str) -> bool:
     return args[3].strip() == "true"
 
 
-def profile(workload: str, outdir: str, steps: int, counter_groups=()):
+def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_warmup: int = 3):
     """Kernel trace plus FETCH_SIZE and WRITE_SIZE passes (each its own run) of the
     benchmark, and one more run per group of extra counters (e.g. SQ_INSTS_VALU);
     writes <workload>.md and .json into outdir (the summaries kept under profiles/
@@ -452,18 +538,22 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=()):
     # benchmark times; the counter passes count bytes, which do not depend on clocks,
     # over `steps` launches.
     cmds = {}
+    traced = {}
     cmds["trace"] = _rocprof(["--workload", workload, "--no-cpu-baseline"], os.path.join(outdir, "trace"),
-                             ["--kernel-trace", "--stats"], env)
+                             ["--kernel-trace", "--stats"], env, traced)
+    tb = traced.get("bench") or {}
     base = ["--workload", workload, "--steps", str(steps), "--warmup", "3", "--no-cpu-baseline", "--copy-calibration"]
     cmds["fetch"] = _rocprof(base, os.path.join(outdir, "fetch"), ["--pmc", "FETCH_SIZE"], env)
     cmds["write"] = _rocprof(base, os.path.join(outdir, "write"), ["--pmc", "WRITE_SIZE"], env)
-    base_nc = [a for a in base if a != "--copy-calibration"]
+    # extra counter passes warm up like the timed run when asked to (instruction counts
+    # depend on the step: early steps take the exact 16-bit parameter path more often)
+    base_nc = ["--workload", workload, "--steps", str(steps), "--warmup", str(counter_warmup), "--no-cpu-baseline"]
     for gi, group in enumerate(counter_groups):
         cmds[f"counters{gi}"] = _rocprof(base_nc, os.path.join(outdir, f"counters{gi}"), ["--pmc", *group], env)
 
     stats = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")]
-    # the dominant step kernel (a multi-tensor step launches one kernel per tensor kind)
-    step_stats = sorted((r for r in stats if "k_step" in r["Name"]), key=lambda r: -float(r["TotalDurationNs"]))
+    # the dominant library kernel (a multi-tensor step launches one kernel per tensor kind)
+    step_stats = sorted((r for r in stats if "bitopt::" in r["Name"]), key=lambda r: -float(r["TotalDurationNs"]))
     kname = step_stats[0]["Name"]
     avg_ns = float(step_stats[0]["AverageNs"])
     calls = int(step_stats[0]["Calls"])
@@ -471,8 +561,8 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=()):
     def counter(name, sub):
         rows = [r for r in _csv_rows(os.path.join(outdir, sub), "counter_collection.csv") if r["Counter_Name"] == name]
         step = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == kname]
-        if not step:      # names spelled differently in the two outputs: any step kernel
-            step = [float(r["Counter_Value"]) for r in rows if "k_step" in r["Kernel_Name"]]
+        if not step:      # names spelled differently in the two outputs: any library kernel
+            step = [float(r["Counter_Value"]) for r in rows if "bitopt::" in r["Kernel_Name"]]
         # the calibration copy is the runtime's device-to-device blit kernel: the
         # dispatches of it with the largest grid
         blits = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
@@ -490,7 +580,7 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=()):
     fetch_b = sum(fs) / len(fs) * f_scale * 1024.0
     write_b = sum(ws) / len(ws) * w_scale * 1024.0
     wl = workload_by_name(workload)
-    if len(wl.tensors) > 1:
+    if len(wl.tensors) > 1 and "k_step" in kname:
         # only the tensors of the dominant kernel's kind (8-bit or 32-bit states)
         quant = kernel_is_8bit(kname)
         wl = W.Workload(**{**wl.__dict__, "tensors": [t for t in wl.tensors if t.eightbit == quant]})
@@ -504,7 +594,7 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=()):
         for name in group:
             per = {}
             for r in rows:
-                if r["Counter_Name"] != name or "k_step" not in r["Kernel_Name"]:
+                if r["Counter_Name"] != name or "bitopt::" not in r["Kernel_Name"]:
                     continue
                 if r["Kernel_Name"] != kname and any(x["Kernel_Name"] == kname for x in rows):
                     continue
@@ -520,6 +610,8 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=()):
                               "write_kib": sum(wc) / len(wc), "fetch_scale": f_scale, "write_scale": w_scale},
          "traffic_bytes_per_launch": fetch_b + write_b, "algorithmic_bytes_per_launch": alg,
          "kernel_elements": kelems, "counters_per_launch": extra,
+         "traced_run": {"ms_per_step": tb.get("ms_per_step"), "value": tb.get("value"), "unit": tb.get("unit"),
+                        "frac": (tb.get("roofline") or {}).get("frac"), "steps": tb.get("steps")},
          "commands": cmds}
     with open(os.path.join(outdir, f"{workload}.json"), "w") as f:
         json.dump(d, f, indent=1)
@@ -529,6 +621,9 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=()):
         f.write("| figure | value |\n|---|---|\n")
         f.write(f"| kernel-trace calls | {calls} |\n")
         f.write(f"| kernel-trace average duration | {avg_ns / 1e3:.2f} us |\n")
+        if tb:
+            f.write(f"| the traced run's own benchmark line: time per step (launch to launch) | "
+                    f"{tb['ms_per_step'] * 1e3:.2f} us ({tb['value']} {tb['unit']}, {tb['roofline']['frac']} of peak) |\n")
         f.write(f"| algorithmic bytes per launch | {alg / 1e6:.1f} MB |\n")
         f.write(f"| algorithmic GB/s at the trace average | {alg / avg_ns:.0f} |\n")
         f.write(f"| FETCH_SIZE per launch (raw) | {sum(fs) / len(fs):.0f} KiB |\n")
@@ -545,7 +640,8 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=()):
                 per_el = v * 64 / kelems if wave else v / kelems
                 f.write(f"| {name} | {v:.6g} | {per_el:.4g} |\n")
             f.write(f"\nElements updated by the kernel per launch: {kelems}.\n\n")
-        pc = f" --profile-counters '{';'.join(','.join(g) for g in counter_groups)}'" if counter_groups else ""
+        pc = (f" --profile-counters '{';'.join(','.join(g) for g in counter_groups)}' --profile-warmup {counter_warmup}"
+              if counter_groups else "")
         f.write(f"Made by `python bench.py --profile <outdir> --workload {workload} --profile-steps {steps}{pc}` "
                 "(from the repository root), which runs the profiler passes below from /tmp with "
                 "TMPDIR=/tmp; raw output stays in the -d directories.  The trace pass is the benchmark's "
@@ -574,10 +670,11 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--profile-counters", default="",
                     help="extra counter passes for --profile: groups separated by ';', counters by ','")
+    ap.add_argument("--profile-warmup", type=int, default=3, help="warm-up launches of the extra counter passes")
     args = ap.parse_args()
     if args.profile:
         groups = [[c for c in g.split(",") if c] for g in args.profile_counters.split(";") if g.strip()]
-        profile(args.workload, args.profile, args.profile_steps, groups)
+        profile(args.workload, args.profile, args.profile_steps, groups, args.profile_warmup)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the optimizer step is per-rank local (blocks are independent), "
@@ -600,7 +697,7 @@ def main():
         t = wl.tensors[0]
         n = t.numel
         step_bytes = workload_bytes(wl)
-        reps = [Replica(wl, r, dev) for r in range(args.replicas)]
+        reps = [(CodecReplica if wl.extra.get("codec") else Replica)(wl, r, dev) for r in range(args.replicas)]
         launchers = None
         if hp.get("skip_zeros"):
             step_bytes = skip_aware_bytes(wl, reps[0].g, step_bytes)
@@ -680,7 +777,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["cpu_baseline"] = (cpu_baseline_codec if wl.extra.get("codec") else cpu_baseline)(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

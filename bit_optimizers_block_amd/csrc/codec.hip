@@ -12,10 +12,8 @@ static hipError_t quant_one(const CodecArgs& a, hipStream_t s) {
 
 template <int DT, int BS>
 static hipError_t dequant_one(const CodecArgs& a, hipStream_t s) {
-    int64_t groups = ((a.n + 3) / 4 + kThreads - 1) / kThreads;
-    if (groups > (1 << 22)) groups = 1 << 22;
-    if (groups < 1) groups = 1;
-    hipLaunchKernelGGL((k_dequantize<DT, BS>), dim3((unsigned)groups), dim3(kThreads), 0, s, a);
+    constexpr int64_t tile = Layout<BS>::TE;
+    hipLaunchKernelGGL((k_dequantize<DT, BS>), tile_grid(a.n, tile), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

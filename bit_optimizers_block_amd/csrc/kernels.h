@@ -1660,29 +1660,48 @@ __global__ __launch_bounds__(kThreads) void k_quantize(CodecArgs a) {
     else quant_tiles<DT, BS, false>(a, M);
 }
 
-// out[i] = qmap[codes[i]] * absmax[i / BS]; each thread handles 4 elements.
+// out[i] = qmap[codes[i]] * absmax[i / BS], in the step kernels' tile layout: a wave
+// owns 4 (B = 256) or 8 (B = 2048) quads, issues the code loads of all of them first,
+// reads each quad's absmax once (uniform), then gathers, scales and stores.
+template <int DT, int BS>
+__device__ __forceinline__ void dequant_tile(const CodecArgs& a, const float* Q, int64_t base, int lane) {
+    using L = Layout<BS>;
+    constexpr int NQ = L::NQ;
+    if (a.vec && base + L::TE <= a.n) {
+        uint32_t w[NQ];
+        float A[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) w[q] = ld_stream(reinterpret_cast<const uint32_t*>(a.codes + L::elem(base, lane, q)));
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) A[q] = gbl(a.absmax)[(base + q * 256) / BS];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = Q[(w[q] >> (8 * i)) & 0xffu] * A[q];
+            store4<DT>(a.out, L::elem(base, lane, q), v);
+        }
+    } else {
+#pragma unroll 1
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t e = L::elem(base, lane, q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (e + i < a.n) store1<DT>(a.out, e + i, Q[gbl(a.codes)[e + i]] * gbl(a.absmax)[(e + i) / BS]);
+        }
+    }
+}
+
 template <int DT, int BS>
 __global__ __launch_bounds__(kThreads) void k_dequantize(CodecArgs a) {
     __shared__ float Q[256];
     Q[threadIdx.x] = gbl(a.qmap)[threadIdx.x];
     __syncthreads();
-    const int64_t nquads = (a.n + 3) / 4;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t qd = (int64_t)blockIdx.x * kThreads + threadIdx.x; qd < nquads; qd += stride) {
-        const int64_t e = qd * 4;
-        const float A = gbl(a.absmax)[e / BS];        // 4 | BS: one block per quad
-        float v[4];
-        if (a.vec && e + 4 <= a.n) {
-            const uint32_t w = ld_stream(reinterpret_cast<const uint32_t*>(a.codes + e));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = Q[(w >> (8 * i)) & 0xffu] * A;
-            store4<DT>(a.out, e, v);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (e + i < a.n) store1<DT>(a.out, e + i, Q[gbl(a.codes)[e + i]] * A);
-        }
-    }
+    constexpr int64_t TE = Layout<BS>::TE;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+    const int64_t ntiles = (a.n + TE - 1) / TE;
+    for (int64_t t = wave_id(); t < ntiles; t += nwaves) dequant_tile<DT, BS>(a, Q, t * TE, lane);
 }
 
 }  // namespace bitopt

@@ -204,6 +204,15 @@ def f4_staged_4096(dtype: str = "f32") -> Workload:
     return w
 
 
+def codec_4096(kind: str = "quantize", dtype: str = "f32", blocksize: int = 256) -> Workload:
+    """The block-wise codec pair on its own: quantize (values -> codes + absmax) or
+    dequantize (codes + absmax -> values) of one 4096x4096 tensor of N(0, 1e-2) values."""
+    return Workload(f"{kind}_blockwise_4096x4096_{dtype}_b{blocksize}", 8,
+                    dict(optimizer="codec", blocksize=blocksize),
+                    [Tensor("x", (4096, 4096), dtype, True)], steps=20, p_scale=0.02, g_scale=1e-2,
+                    extra={"codec": kind})
+
+
 def adam_small_1024x9() -> Workload:
     """The pages' small benchmark shape (1024 x 9 fp32, Adam 8-bit), where the step
     is launch-bound rather than bandwidth-bound."""

@@ -427,6 +427,9 @@ def test_codec_unaligned_and_empty():
     codes, absmax = bitopt.quantize_blockwise(xd, qd, bs, codes=cbuf[1:])
     np.testing.assert_array_equal(to_host(codes), codes_ref)
     np.testing.assert_array_equal(to_host(absmax), absmax_ref)
+    obuf = torch.zeros(n + 1, device="cuda")           # codes and output both off their vector alignment
+    out = bitopt.dequantize_blockwise(codes, absmax, qd, bs, out=obuf[1:n])
+    np.testing.assert_array_equal(to_host(out), oracle.dequantize_blockwise(codes_ref, absmax_ref, qmap, bs, "f32"))
     e = torch.zeros(0, device="cuda")
     bitopt.quantize_blockwise(e, qd, bs)
     bitopt.dequantize_blockwise(torch.zeros(0, dtype=torch.uint8, device="cuda"),
