@@ -55,6 +55,8 @@ def workload_by_name(name):
         "adamw_bf16_tensorwise": lambda: W.f3_tensorwise_4096("bf16"),
         "adamw_fp32_b256_paged": lambda: W.f4_paged_4096("f32"),
         "adamw_fp32_b256_staged": lambda: W.f4_staged_4096("f32"),
+        "adamw_fp32_b256_pooled": lambda: W.f4_pooled_4096("f32", 1 << 23, 2),
+        "adamw_fp32_b256_pooled_thrash": lambda: W.f4_pooled_4096("f32", 1 << 22, 2),
         "adam_fp32_256x256": W.c1_adam_256,
         "adam_fp32_1024x9": W.adam_small_1024x9,
         "adamw32_fp32_4096": lambda: W.adamw_32bit_4096("f32"),
@@ -245,6 +247,10 @@ class Replica:
             self.staging = torch.empty(bitopt.paged_staging_bytes(hp, wl.extra["chunk"]), dtype=torch.uint8,
                                        device=dev)
             self.copy_streams = (torch.cuda.Stream(), torch.cuda.Stream())
+        self.pool = None
+        if wl.extra.get("paged") == "pooled":
+            # host-resident state behind an HBM page pool
+            self.pool = bitopt.PagePool(hp, wl.extra["page"], nframes=wl.extra["frames"], device=dev)
         if wl.extra.get("paged"):
             # optimizer state in pinned host memory mapped into the GPU address space
             def z(numel, dt):
@@ -261,6 +267,9 @@ class Replica:
         self.a2 = z(nb, torch.float32) if (self.two and self.eightbit) else None
 
     def step(self, hp, t, q1, q2):
+        if self.pool is not None:
+            self.pool.step(hp, t, self.p, self.g, self.s1, self.a1, q1, self.s2, self.a2, q2 if self.two else None)
+            return
         if self.staged:
             bitopt.step_8bit_paged(hp, t, self.p, self.g, self.s1, self.a1, q1, self.s2, self.a2,
                                    q2 if self.two else None, staging=self.staging, h2d_stream=self.copy_streams[0],
@@ -289,7 +298,13 @@ class Replica:
         dt = bitopt.DTYPES[self.p.dtype]
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         opt = lambda x: None if x is None else ptr(x)
-        if self.staged:
+        head = (ctypes.byref(h), )
+        if self.pool is not None:
+            f = L.bitopt_step_8bit_pooled
+            head = (self.pool.handle, ctypes.byref(h))
+            tail = (ptr(self.s1), opt(self.s2), ptr(self.a1), opt(self.a2), ptr(q1), ptr(q2) if self.two else None,
+                    stream)
+        elif self.staged:
             f = L.bitopt_step_8bit_paged
             tail = (ptr(self.s1), opt(self.s2), ptr(self.a1), opt(self.a2), ptr(q1), ptr(q2) if self.two else None,
                     ptr(self.staging), self.staging.numel(), ctypes.c_void_p(self.copy_streams[0].cuda_stream),
@@ -307,7 +322,6 @@ class Replica:
         else:
             f = L.bitopt_step_8bit_blockwise_1state
             tail = (ptr(self.s1), ptr(self.a1), ptr(q1), stream)
-        head = (ctypes.byref(h), )
         mid = (ptr(self.p), ptr(self.g), dt, self.n)
         self._keep = h
 
@@ -757,7 +771,10 @@ def main():
                "param_dtype": t.dtype, "blocksize": B, "weight_decay": hp.get("weight_decay", 0.0),
                "skip_zeros": bool(hp.get("skip_zeros", False)), "replicas": len(reps),
                "arithmetic": "f32", "state_dtype": "u8" if t.eightbit else "f32"}
-        if wl.extra.get("paged") == "staged":
+        if wl.extra.get("paged") == "pooled":
+            cfg["state_memory"] = (f"pinned host, cached in an HBM page pool of {wl.extra['frames']} frames of "
+                                   f"{wl.extra['page']} elements")
+        elif wl.extra.get("paged") == "staged":
             cfg["state_memory"] = f"pinned host, paged through HBM staging in chunks of {wl.extra['chunk']} elements"
         elif wl.extra.get("paged"):
             cfg["state_memory"] = "pinned host, read and written in place over the host link"

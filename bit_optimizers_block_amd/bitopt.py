@@ -122,6 +122,12 @@ def lib():
             "bitopt_tensorwise_scratch_bytes": ([], i64),
             "bitopt_paged_staging_bytes": ([HP, i64], i64),
             "bitopt_step_8bit_paged": ([HP, i32, P, P, i32, i64, P, P, P, P, P, P, P, i64, P, P, P], ctypes.c_int),
+            "bitopt_page_pool_frame_bytes": ([HP, i64], i64),
+            "bitopt_page_pool_create": ([HP, i64, P, i64, ctypes.POINTER(P)], ctypes.c_int),
+            "bitopt_page_pool_destroy": ([P], ctypes.c_int),
+            "bitopt_step_8bit_pooled": ([P, HP, i32, P, P, i32, i64, P, P, P, P, P, P, P], ctypes.c_int),
+            "bitopt_page_pool_flush": ([P, i32, P], ctypes.c_int),
+            "bitopt_page_pool_stats": ([P, ctypes.POINTER(i64)], ctypes.c_int),
             "bitopt_step_multi": ([HP, i32, ctypes.POINTER(Tensor), i32, P, P, P, i64, P], ctypes.c_int),
             "bitopt_multi_plan_build": ([HP, ctypes.POINTER(Tensor), i32, P, i64, ctypes.POINTER(MultiPlanC), P],
                                         ctypes.c_int),
@@ -371,6 +377,75 @@ def step_8bit_paged(hp, step, p, g, state1, absmax1, qmap1, state2=None, absmax2
                                         _ptr(staging), staging.numel(), _stream(h2d_stream), _stream(d2h_stream),
                                         _stream(stream)))
     return staging
+
+
+def page_pool_frame_bytes(hp, page_elems: int) -> int:
+    return lib().bitopt_page_pool_frame_bytes(ctypes.byref(make_hparams(hp)), int(page_elems))
+
+
+class PagePool:
+    """An HBM page pool in front of host-resident 8-bit state (bitopt_page_pool_*):
+    pages stay in its frames while they fit and are written back and replaced, least
+    recently used first, when they do not.  `frames` is a device uint8 tensor (made
+    for `nframes` frames when not given); the pool keeps it alive."""
+
+    def __init__(self, hp, page_elems: int, nframes: int = None, frames=None, device="cuda"):
+        self.hp = dict(hp)
+        fb = page_pool_frame_bytes(hp, page_elems)
+        if fb < 0:
+            raise ValueError(f"invalid page pool arguments (page_elems={page_elems})")
+        if frames is None:
+            frames = torch.empty(fb * int(nframes), dtype=torch.uint8, device=device)
+        self.frames = frames
+        self.page_elems = int(page_elems)
+        self.frame_bytes = fb
+        h = ctypes.c_void_p()
+        _check(lib().bitopt_page_pool_create(ctypes.byref(make_hparams(hp)), self.page_elems, _ptr(frames),
+                                             frames.numel() * frames.element_size(), ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("the page pool is closed")
+        return self._h
+
+    def step(self, hp, step, p, g, state1, absmax1, qmap1, state2=None, absmax2=None, qmap2=None, stream=None):
+        """One 8-bit step on host_state() buffers through the pool."""
+        h = make_hparams(hp)
+        n = p.numel()
+        k = 2 if h.optimizer == OPTIMIZERS["ademamix"] else 1
+        two = h.optimizer in (OPTIMIZERS["adam"], OPTIMIZERS["ademamix"])
+        nb = nblocks(n, h.blocksize)
+        _need(p, "p"); _need(g, "g", p.dtype, n)
+        for t, name, dt, cnt in ((state1, "state1", torch.uint8, k * n),
+                                 (absmax1, "absmax1", torch.float32, k * nb)) + (
+                ((state2, "state2", torch.uint8, n), (absmax2, "absmax2", torch.float32, nb)) if two else ()):
+            _need(t, name, dt, cnt, device=False)
+            if t.is_cuda:
+                raise ValueError(f"{name} must be host memory (host_state())")
+        _check(lib().bitopt_step_8bit_pooled(self.handle, ctypes.byref(h), int(step), _ptr(p), _ptr(g), _dt(p), n,
+                                             _ptr(state1), _ptr(state2), _ptr(absmax1), _ptr(absmax2), _ptr(qmap1),
+                                             _ptr(qmap2), _stream(stream)))
+
+    def flush(self, evict: bool = False, stream=None):
+        _check(lib().bitopt_page_pool_flush(self.handle, 1 if evict else 0, _stream(stream)))
+
+    def stats(self) -> dict:
+        out = (ctypes.c_int64 * 4)()
+        _check(lib().bitopt_page_pool_stats(self.handle, out))
+        return dict(resident=out[0], page_ins=out[1], write_backs=out[2], hits=out[3])
+
+    def close(self):
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check(lib().bitopt_page_pool_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def multi_workspace_bytes(count: int) -> int:

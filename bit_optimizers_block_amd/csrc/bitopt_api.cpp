@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "bitopt.h"
@@ -471,6 +473,351 @@ int bitopt_step_8bit_paged(const bitopt_hparams* hp, int32_t step, void* p, cons
 }
 
 }  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- paged state, cached in an HBM page pool
+
+// One frame of the pool: room for one page (the state of page_elems elements of one
+// tensor, in the staging layout), the identity of the page it holds and the events
+// that order its copies and steps.
+struct PoolFrame {
+    const uint8_t* key = nullptr;      // host_state1 of the owning tensor (nullptr: free)
+    int64_t page = 0;                  // page index inside that tensor
+    uint8_t* hs1 = nullptr;            // the owner's host buffers and size (write-back targets)
+    uint8_t* hs2 = nullptr;
+    float* ha1 = nullptr;
+    float* ha2 = nullptr;
+    int64_t n = 0;
+    bool dirty = false;                // stepped since it was copied in or last written back
+    uint64_t tick = 0;                 // last use (least recently used frame is evicted first)
+    hipStream_t last_stream = nullptr; // stream of its last step
+    hipEvent_t in = nullptr;           // copy-in complete
+    hipEvent_t comp = nullptr;         // last step on it complete
+    bool stepped = false;              // comp has been recorded
+    bool wb_pending = false;           // written back since its last step; a step must first wait for tail
+};
+
+struct PageKeyHash {
+    size_t operator()(const std::pair<const uint8_t*, int64_t>& k) const {
+        return std::hash<const void*>()(k.first) ^ (std::hash<int64_t>()(k.second) * 0x9E3779B97F4A7C15ull);
+    }
+};
+
+}  // namespace
+
+struct bitopt_page_pool {
+    int device = 0;
+    int32_t optimizer = 0, blocksize = 0;
+    int64_t C = 0;                     // page size in elements
+    StageLayout L{};
+    uint8_t* frames = nullptr;
+    std::vector<PoolFrame> fr;
+    std::unordered_map<std::pair<const uint8_t*, int64_t>, int, PageKeyHash> where;
+    hipStream_t h2d = nullptr, d2h = nullptr;   // the pool's own copy streams (default priority)
+    hipEvent_t tail = nullptr;                  // recorded on d2h after every write-back
+    uint64_t tail_seq = 0, h2d_seen = 0;        // records of tail; the last one h2d waited for
+    hipEvent_t start = nullptr;
+    uint64_t tick = 0;
+    int64_t page_ins = 0, write_backs = 0, hits = 0;
+};
+
+namespace {
+
+int pool_device_ok(const bitopt_page_pool* pool, const char* fn) {
+    int dev = -1;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return device_status(e, fn);
+    if (dev != pool->device)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: the pool was created on device %d, the current device is %d", fn,
+                    pool->device, dev);
+    return BITOPT_OK;
+}
+
+// Enqueues the write-back of frame f's page to its owner's host buffers on the pool's
+// d2h stream (after the frame's last step, when that ran on a stream other than
+// `after`, whose own order the caller has already joined to d2h).
+hipError_t pool_write_back(bitopt_page_pool* pool, PoolFrame& F, hipStream_t after) {
+    const int64_t B = pool->blocksize, C = pool->C;
+    const bool two = pool->optimizer == BITOPT_ADAM || pool->optimizer == BITOPT_ADEMAMIX;
+    const int64_t k1 = pool->optimizer == BITOPT_ADEMAMIX ? 2 : 1;
+    const int64_t c0 = F.page * C, len = std::min(C, F.n - c0);
+    const int64_t nb = (F.n + B - 1) / B, cb0 = c0 / B, nbc = (len + B - 1) / B;
+    uint8_t* buf = pool->frames + (&F - pool->fr.data()) * pool->L.bytes;
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    if (F.last_stream != after) chk(hipStreamWaitEvent(pool->d2h, F.comp, 0));
+    for (int64_t k = 0; k < k1; ++k) {
+        chk(hipMemcpyAsync(F.hs1 + k * F.n + c0, buf + pool->L.s1 + k * len, len, hipMemcpyDeviceToHost, pool->d2h));
+        chk(hipMemcpyAsync(F.ha1 + k * nb + cb0, buf + pool->L.a1 + 4 * k * nbc, 4 * nbc, hipMemcpyDeviceToHost,
+                           pool->d2h));
+    }
+    if (two) {
+        chk(hipMemcpyAsync(F.hs2 + c0, buf + pool->L.s2, len, hipMemcpyDeviceToHost, pool->d2h));
+        chk(hipMemcpyAsync(F.ha2 + cb0, buf + pool->L.a2, 4 * nbc, hipMemcpyDeviceToHost, pool->d2h));
+    }
+    F.dirty = false;
+    F.wb_pending = true;
+    ++pool->write_backs;
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bitopt_page_pool_frame_bytes(const bitopt_hparams* hp, int64_t page_elems) {
+    if (!hp || page_elems < 1 || page_elems % kPageQuantum != 0 || !valid_blocksize(hp->blocksize) ||
+        hp->optimizer < BITOPT_ADAM || hp->optimizer > BITOPT_ADAGRAD)
+        return -1;
+    return stage_layout(hp->optimizer, hp->blocksize, page_elems).bytes;
+}
+
+int bitopt_page_pool_create(const bitopt_hparams* hp, int64_t page_elems, void* frames, int64_t frames_bytes,
+                            bitopt_page_pool** pool) {
+    const char* fn = "bitopt_page_pool_create";
+    if (!pool) return fail(BITOPT_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+    *pool = nullptr;
+    if (int rc = check_hparams(hp, 1, 0, fn)) return rc;
+    if (page_elems < kPageQuantum || page_elems % kPageQuantum != 0)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: page_elems must be a positive multiple of %lld (got %lld)", fn,
+                    (long long)kPageQuantum, (long long)page_elems);
+    if (!frames) return fail(BITOPT_ERR_INVALID_ARG, "%s: frames is NULL", fn);
+    if (!aligned(frames, kStageAlign)) return fail(BITOPT_ERR_INVALID_ARG, "%s: frames not 256-byte aligned", fn);
+    const StageLayout L = stage_layout(hp->optimizer, hp->blocksize, page_elems);
+    const int64_t nframes = frames_bytes / L.bytes;
+    if (nframes < 2)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: %lld bytes hold %lld frames of %lld bytes; at least 2 are needed", fn,
+                    (long long)frames_bytes, (long long)nframes, (long long)L.bytes);
+    if (nframes > (int64_t)1 << 20) return fail(BITOPT_ERR_INVALID_ARG, "%s: more than 2^20 frames", fn);
+    auto* P = new bitopt_page_pool;
+    P->optimizer = hp->optimizer;
+    P->blocksize = hp->blocksize;
+    P->C = page_elems;
+    P->L = L;
+    P->frames = static_cast<uint8_t*>(frames);
+    P->fr.resize((size_t)nframes);
+    hipError_t e = hipGetDevice(&P->device);
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    chk(hipStreamCreateWithFlags(&P->h2d, hipStreamNonBlocking));
+    chk(hipStreamCreateWithFlags(&P->d2h, hipStreamNonBlocking));
+    chk(hipEventCreateWithFlags(&P->tail, hipEventDisableTiming));
+    chk(hipEventCreateWithFlags(&P->start, hipEventDisableTiming));
+    for (PoolFrame& F : P->fr) {
+        chk(hipEventCreateWithFlags(&F.in, hipEventDisableTiming));
+        chk(hipEventCreateWithFlags(&F.comp, hipEventDisableTiming));
+    }
+    if (e != hipSuccess) {
+        (void)bitopt_page_pool_destroy(P);
+        return device_status(e, fn);
+    }
+    *pool = P;
+    return ok();
+}
+
+int bitopt_page_pool_destroy(bitopt_page_pool* pool) {
+    if (!pool) return ok();
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    // the pool's copies may still read or write frames and host buffers
+    if (pool->h2d) chk(hipStreamSynchronize(pool->h2d));
+    if (pool->d2h) chk(hipStreamSynchronize(pool->d2h));
+    for (PoolFrame& F : pool->fr) {
+        if (F.comp && F.stepped) chk(hipEventSynchronize(F.comp));
+        if (F.in) chk(hipEventDestroy(F.in));
+        if (F.comp) chk(hipEventDestroy(F.comp));
+    }
+    if (pool->tail) chk(hipEventDestroy(pool->tail));
+    if (pool->start) chk(hipEventDestroy(pool->start));
+    if (pool->h2d) chk(hipStreamDestroy(pool->h2d));
+    if (pool->d2h) chk(hipStreamDestroy(pool->d2h));
+    delete pool;
+    return device_status(e, "bitopt_page_pool_destroy");
+}
+
+int bitopt_step_8bit_pooled(bitopt_page_pool* pool, const bitopt_hparams* hp, int32_t step, void* p, const void* g,
+                            int32_t dtype, int64_t n, uint8_t* host_state1, uint8_t* host_state2,
+                            float* host_absmax1, float* host_absmax2, const float* qmap1, const float* qmap2,
+                            void* stream) {
+    const char* fn = "bitopt_step_8bit_pooled";
+    if (!pool) return fail(BITOPT_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+    if (int rc = check_hparams(hp, step, n, fn)) return rc;
+    if (hp->optimizer != pool->optimizer || hp->blocksize != pool->blocksize)
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: the pool holds optimizer %d, blocksize %d state (got %d, %d)", fn,
+                    pool->optimizer, pool->blocksize, hp->optimizer, hp->blocksize);
+    if (!valid_dtype(dtype)) return fail(BITOPT_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    const bool two = hp->optimizer == BITOPT_ADAM || hp->optimizer == BITOPT_ADEMAMIX;
+    if (n == 0) return ok();
+    if (!p || !g || !host_state1 || !host_absmax1 || !qmap1 || (two && (!host_state2 || !host_absmax2 || !qmap2)))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!two) { host_state2 = nullptr; host_absmax2 = nullptr; }
+    if (int rc = pool_device_ok(pool, fn)) return rc;
+    const int64_t C = pool->C, B = hp->blocksize;
+    const int64_t npages = (n + C - 1) / C;
+    // every page of this tensor already in the pool must belong to the same buffers
+    for (int64_t i = 0; i < npages; ++i) {
+        auto it = pool->where.find({host_state1, i});
+        if (it == pool->where.end()) continue;
+        const PoolFrame& F = pool->fr[(size_t)it->second];
+        if (F.n != n || F.hs2 != host_state2 || F.ha1 != host_absmax1 || F.ha2 != host_absmax2)
+            return fail(BITOPT_ERR_INVALID_ARG,
+                        "%s: host_state1 is in the pool with other companion buffers or size; flush with evict first",
+                        fn);
+    }
+    hipStream_t sc = reinterpret_cast<hipStream_t>(stream);
+    const int64_t k1 = hp->optimizer == BITOPT_ADEMAMIX ? 2 : 1;
+    const int64_t nb = (n + B - 1) / B;
+    const int es = elem_size(dtype);
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    const uint64_t call_start = pool->tick + 1;   // frames stepped by this call have tick >= call_start
+    // At the first page that is not resident, `start` is recorded on sc: the copy-in stream
+    // waits for it (host state written by work already on sc, e.g. another pool's flush, is
+    // read only after it) and so does the write-back stream (pages stepped on sc so far).
+    bool started = false, h2d_joined = false, d2h_joined = false;
+    bool waited_tail = false;               // sc ordered after every write-back enqueued so far
+    auto start = [&]() {
+        if (!started) {
+            chk(hipEventRecord(pool->start, sc));
+            started = true;
+        }
+    };
+    for (int64_t i = 0; i < npages && e == hipSuccess; ++i) {
+        const int64_t c0 = i * C, len = std::min(C, n - c0);
+        const int64_t cb0 = c0 / B, nbc = (len + B - 1) / B;
+        int f;
+        auto it = pool->where.find({host_state1, i});
+        if (it != pool->where.end()) {
+            f = it->second;
+            PoolFrame& F = pool->fr[(size_t)f];
+            if (F.last_stream != sc) chk(hipStreamWaitEvent(sc, F.comp, 0));
+            if (F.wb_pending) {              // a flush's write-back may still read the frame
+                if (!waited_tail) chk(hipStreamWaitEvent(sc, pool->tail, 0));
+                waited_tail = true;
+                F.wb_pending = false;
+            }
+            ++pool->hits;
+        } else {
+            // a free frame, else the least recently used one (pages this call has stepped
+            // are the most recent, so they go last)
+            f = -1;
+            for (size_t j = 0; j < pool->fr.size(); ++j) {
+                const PoolFrame& F = pool->fr[j];
+                if (!F.key) { f = (int)j; break; }
+                if (f < 0 || F.tick < pool->fr[(size_t)f].tick) f = (int)j;
+            }
+            PoolFrame& F = pool->fr[(size_t)f];
+            start();
+            if (F.key) {
+                if (F.dirty) {
+                    if (!d2h_joined) {     // one wait covers every earlier step on sc
+                        chk(hipStreamWaitEvent(pool->d2h, pool->start, 0));
+                        d2h_joined = true;
+                    }
+                    if (F.last_stream == sc && F.tick >= call_start) {
+                        // stepped in this call, possibly after `start`: wait for that step itself
+                        chk(hipStreamWaitEvent(pool->d2h, F.comp, 0));
+                    }
+                    chk(pool_write_back(pool, F, sc));
+                    chk(hipEventRecord(pool->tail, pool->d2h));
+                    ++pool->tail_seq;
+                }
+                pool->where.erase({F.key, F.page});
+                F.key = nullptr;
+            }
+            uint8_t* buf = pool->frames + (int64_t)f * pool->L.bytes;
+            if (!h2d_joined) {
+                chk(hipStreamWaitEvent(pool->h2d, pool->start, 0));
+                h2d_joined = true;
+            }
+            // the host copy is current only once every write-back enqueued so far is done
+            if (pool->h2d_seen != pool->tail_seq) {
+                chk(hipStreamWaitEvent(pool->h2d, pool->tail, 0));
+                pool->h2d_seen = pool->tail_seq;
+            }
+            for (int64_t k = 0; k < k1; ++k) {
+                chk(hipMemcpyAsync(buf + pool->L.s1 + k * len, host_state1 + k * n + c0, len, hipMemcpyHostToDevice,
+                                   pool->h2d));
+                chk(hipMemcpyAsync(buf + pool->L.a1 + 4 * k * nbc, host_absmax1 + k * nb + cb0, 4 * nbc,
+                                   hipMemcpyHostToDevice, pool->h2d));
+            }
+            if (two) {
+                chk(hipMemcpyAsync(buf + pool->L.s2, host_state2 + c0, len, hipMemcpyHostToDevice, pool->h2d));
+                chk(hipMemcpyAsync(buf + pool->L.a2, host_absmax2 + cb0, 4 * nbc, hipMemcpyHostToDevice, pool->h2d));
+            }
+            chk(hipEventRecord(F.in, pool->h2d));
+            chk(hipStreamWaitEvent(sc, F.in, 0));
+            F.key = host_state1;
+            F.page = i;
+            F.hs1 = host_state1; F.hs2 = host_state2; F.ha1 = host_absmax1; F.ha2 = host_absmax2;
+            F.n = n;
+            F.dirty = false;
+            F.wb_pending = false;            // the copy-in followed every write-back (tail)
+            pool->where[{host_state1, i}] = f;
+            ++pool->page_ins;
+        }
+        if (e != hipSuccess) break;
+        PoolFrame& F = pool->fr[(size_t)f];
+        uint8_t* buf = pool->frames + (int64_t)f * pool->L.bytes;
+        if (int rc = run_step(hp, step, static_cast<uint8_t*>(p) + c0 * es, static_cast<const uint8_t*>(g) + c0 * es,
+                              dtype, len, buf + pool->L.s1, two ? buf + pool->L.s2 : nullptr,
+                              reinterpret_cast<float*>(buf + pool->L.a1),
+                              two ? reinterpret_cast<float*>(buf + pool->L.a2) : nullptr, qmap1,
+                              two ? qmap2 : nullptr, true, stream, fn))
+            return rc;
+        chk(hipEventRecord(F.comp, sc));
+        F.stepped = true;
+        F.last_stream = sc;
+        F.dirty = true;
+        F.tick = ++pool->tick;
+    }
+    return device_status(e, fn);
+}
+
+int bitopt_page_pool_flush(bitopt_page_pool* pool, int32_t evict, void* stream) {
+    const char* fn = "bitopt_page_pool_flush";
+    if (!pool) return fail(BITOPT_ERR_INVALID_ARG, "%s: pool is NULL", fn);
+    if (int rc = pool_device_ok(pool, fn)) return rc;
+    hipStream_t sc = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    bool any = false;
+    for (PoolFrame& F : pool->fr) {
+        if (!F.key || !F.dirty) continue;
+        if (!any) {
+            chk(hipEventRecord(pool->start, sc));
+            chk(hipStreamWaitEvent(pool->d2h, pool->start, 0));
+            any = true;
+        }
+        chk(pool_write_back(pool, F, sc));
+    }
+    if (any) {
+        chk(hipEventRecord(pool->tail, pool->d2h));
+        ++pool->tail_seq;
+    }
+    // `stream` completes only after every write-back enqueued so far
+    if (pool->tail_seq) chk(hipStreamWaitEvent(sc, pool->tail, 0));
+    if (evict) {
+        for (PoolFrame& F : pool->fr) {
+            // a later copy-in into this frame waits for `tail`, which follows its last step
+            F.key = nullptr;
+            F.dirty = false;
+        }
+        pool->where.clear();
+    }
+    return device_status(e, fn);
+}
+
+int bitopt_page_pool_stats(const bitopt_page_pool* pool, int64_t* out4) {
+    if (!pool || !out4) return fail(BITOPT_ERR_INVALID_ARG, "bitopt_page_pool_stats: NULL pointer");
+    out4[0] = (int64_t)pool->where.size();
+    out4[1] = pool->page_ins;
+    out4[2] = pool->write_backs;
+    out4[3] = pool->hits;
+    return ok();
+}
+
+}  // extern "C"
+
 
 namespace {
 

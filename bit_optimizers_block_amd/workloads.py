@@ -204,6 +204,17 @@ def f4_staged_4096(dtype: str = "f32") -> Workload:
     return w
 
 
+def f4_pooled_4096(dtype: str = "f32", page: int = 1 << 23, frames: int = 2) -> Workload:
+    """The block-wise AdamW workload with the state in pinned host memory behind an HBM
+    page pool of `frames` frames of `page` elements: with room for every page the state
+    stays resident after the first step; with fewer frames every step pages it through."""
+    w = c2_adamw_4096(dtype, 256)
+    pages = -(-w.tensors[0].numel // page)
+    w.name = f"adamw8bit_4096x4096_{dtype}_b256_pooled_{'resident' if frames >= pages else f'{frames}of{pages}'}"
+    w.extra = {"paged": "pooled", "page": page, "frames": frames}
+    return w
+
+
 def codec_4096(kind: str = "quantize", dtype: str = "f32", blocksize: int = 256) -> Workload:
     """The block-wise codec pair on its own: quantize (values -> codes + absmax) or
     dequantize (codes + absmax -> values) of one 4096x4096 tensor of N(0, 1e-2) values."""

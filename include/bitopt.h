@@ -320,6 +320,75 @@ BITOPT_API int bitopt_step_8bit_paged(const bitopt_hparams* hp, int32_t step, vo
                                       const float* qmap2, void* staging, int64_t staging_bytes,
                                       void* h2d_stream, void* d2h_stream, void* stream);
 
+/*
+ * Paged state, cached: an HBM page pool in front of host-resident 8-bit state (the
+ * optimizer overview's is_paged and the 8-bit PR's Paged*8bit optimizers keep state in
+ * memory that lives on the GPU while it fits and moves to host memory under pressure;
+ * here the library does that paging explicitly).  A page is the state of one range of
+ * page_elems elements of one tensor (its codes and absmax, the layout of a staging
+ * chunk); a frame is HBM room for one page.  A pooled step looks every page of its
+ * tensor up (key: host_state1 and the page index): a resident page is stepped where it
+ * lies; a missing one takes a free frame or the least recently used one (whose page is
+ * first written back to its host buffers if stepped since), is copied in, then stepped.
+ * When every page fits, steps after the first copy nothing and run at the speed of the
+ * device-resident step; when they do not, each step pages its state through the frames.
+ * Results are bit-identical to the device-resident step.  The host buffers are current
+ * only after bitopt_page_pool_flush (and its stream's completion).
+ *
+ * Copies run on two streams the pool owns (default priority), ordered by events
+ * against the step streams; no call waits on the host.  A pool is not thread-safe: one
+ * host thread at a time.  It belongs to the device current at its creation.
+ */
+typedef struct bitopt_page_pool bitopt_page_pool;
+
+/* Bytes of one frame for pages of page_elems elements (a positive multiple of 4096), or
+ * < 0 for invalid arguments. */
+BITOPT_API int64_t bitopt_page_pool_frame_bytes(const bitopt_hparams* hp, int64_t page_elems);
+
+/*
+ *   hp           optimizer and blocksize of every tensor the pool will hold (fixes the
+ *                page layout); the other fields are not used
+ *   page_elems   a positive multiple of 4096
+ *   frames       device, 256-byte aligned, frames_bytes long, caller-owned; holds
+ *                floor(frames_bytes / frame_bytes) frames, at least 2 (at most 2^20).
+ *                In use by the pool until bitopt_page_pool_destroy returns
+ *   *pool        receives the pool (a host object)
+ * Errors: INVALID_ARG for the above; DEVICE if its streams or events cannot be made.
+ */
+BITOPT_API int bitopt_page_pool_create(const bitopt_hparams* hp, int64_t page_elems, void* frames,
+                                       int64_t frames_bytes, bitopt_page_pool** pool);
+/* Waits for the pool's copies, then releases its streams, events and host object.
+ * Writes nothing back: flush first to keep the state.  NULL is accepted. */
+BITOPT_API int bitopt_page_pool_destroy(bitopt_page_pool* pool);
+
+/*
+ * One 8-bit block-wise step (2-state or 1-state, as bitopt_step_8bit_blockwise_*) on a
+ * tensor whose state lives in host buffers (bitopt_host_state_alloc or other pinned
+ * memory, laid out as the device-resident call's state1/2, absmax1/2; state2, absmax2,
+ * qmap2 NULL for 1-state optimizers), through `pool`.  p, g, qmap1/2: device.  Work
+ * already on `stream` (e.g. the gradient) precedes the step; calls enqueue and return.
+ * A host_state1 already in the pool must come with the same companion buffers and n.
+ * Host buffers of different tensors must not overlap.  Before host buffers are freed
+ * or reused for another tensor, flush with evict = 1.
+ * Errors: as the per-tensor calls; INVALID_ARG when hp's optimizer or blocksize differs
+ * from the pool's, for another current device, or for mismatched companion buffers.
+ * After a DEVICE error the pool's bookkeeping is undefined: destroy it.
+ */
+BITOPT_API int bitopt_step_8bit_pooled(bitopt_page_pool* pool, const bitopt_hparams* hp, int32_t step, void* p,
+                                       const void* g, int32_t dtype, int64_t n, uint8_t* host_state1,
+                                       uint8_t* host_state2, float* host_absmax1, float* host_absmax2,
+                                       const float* qmap1, const float* qmap2, void* stream);
+
+/*
+ * Writes every page stepped since its last write-back to its host buffers; `stream`
+ * completes only after all of them (work already on `stream` precedes them).  evict
+ * != 0 also empties the pool (the next step on any tensor copies its state in again).
+ */
+BITOPT_API int bitopt_page_pool_flush(bitopt_page_pool* pool, int32_t evict, void* stream);
+
+/* out4 = {resident pages, page-ins, write-backs, resident hits} since creation. */
+BITOPT_API int bitopt_page_pool_stats(const bitopt_page_pool* pool, int64_t* out4);
+
 /* Bytes of device workspace a multi-tensor step needs for `count` tensors (< 0 if count < 0). */
 BITOPT_API int64_t bitopt_multi_workspace_bytes(int32_t count);
 

@@ -218,3 +218,34 @@ def test_multi_plan_argument_errors(B):
     assert L.bitopt_step_multi_planned(ctypes.byref(empty), ctypes.byref(h3), 1, None, None, None) == E
     assert L.bitopt_step_multi_planned(ctypes.byref(empty), ctypes.byref(h), 0, None, None, None) == E   # step 0
     assert L.bitopt_step_multi_planned(None, ctypes.byref(h), 1, None, None, None) == E
+
+
+def test_page_pool_argument_errors(B):
+    """The page-pool calls on their argument-checking paths (no pool is made: every
+    refusal here comes before the first device call)."""
+    L = B.lib()
+    E = B.ERR_INVALID_ARG
+    h = B.make_hparams(dict(optimizer="adam", blocksize=256))
+    fb = L.bitopt_page_pool_frame_bytes(ctypes.byref(h), 4096)
+    assert fb >= 2 * 4096 + 2 * 4 * 16                               # two code arrays and two absmax arrays
+    assert fb % 256 == 0
+    assert L.bitopt_page_pool_frame_bytes(ctypes.byref(h), 4000) < 0      # not a multiple of 4096
+    assert L.bitopt_page_pool_frame_bytes(ctypes.byref(h), 0) < 0
+    assert L.bitopt_page_pool_frame_bytes(None, 4096) < 0
+    hm = B.make_hparams(dict(optimizer="momentum", blocksize=2048))
+    assert 4096 <= L.bitopt_page_pool_frame_bytes(ctypes.byref(hm), 4096) < fb   # one state
+    pool = ctypes.c_void_p()
+    F = ctypes.c_void_p(1 << 20)
+    assert L.bitopt_page_pool_create(ctypes.byref(h), 4096, F, 2 * fb, None) == E
+    assert L.bitopt_page_pool_create(ctypes.byref(h), 4000, F, 2 * fb, ctypes.byref(pool)) == E
+    assert "multiple" in B.last_error() and not pool.value
+    assert L.bitopt_page_pool_create(ctypes.byref(h), 4096, None, 2 * fb, ctypes.byref(pool)) == E
+    assert L.bitopt_page_pool_create(ctypes.byref(h), 4096, ctypes.c_void_p((1 << 20) + 64), 2 * fb,
+                                     ctypes.byref(pool)) == E
+    assert L.bitopt_page_pool_create(ctypes.byref(h), 4096, F, 2 * fb - 1, ctypes.byref(pool)) == E
+    assert "at least 2" in B.last_error()
+    P = ctypes.c_void_p(16)
+    assert L.bitopt_step_8bit_pooled(None, ctypes.byref(h), 1, P, P, 0, 16, P, P, P, P, P, P, None) == E
+    assert L.bitopt_page_pool_flush(None, 0, None) == E
+    assert L.bitopt_page_pool_stats(None, (ctypes.c_int64 * 4)()) == E
+    assert L.bitopt_page_pool_destroy(None) == B.OK

@@ -189,3 +189,119 @@ def test_staged_paged_argument_errors():
     with pytest.raises(bitopt.BitoptError, match="distinct"):
         bitopt.step_8bit_paged(hp, 1, p, p, s1, a1, q, s2, a2, q, staging=ok, h2d_stream=st[0], d2h_stream=st[0])
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ paged state in an HBM page pool
+# bitopt_step_8bit_pooled: host-resident state cached page by page in HBM frames;
+# resident pages are stepped in place, missing ones are copied in after the least
+# recently used frame is written back.  Host buffers are current after a flush.
+
+def _pooled_step(pool, q, t, g_dev, stream=None):
+    d = q.d
+    pool.step(q.hp, t, d["p"], g_dev, d["s1"], d["a1"], d["q1"], d.get("s2"), d.get("a2"),
+              d["q2"] if q.two else None, stream=stream)
+
+
+@pytest.mark.parametrize("name,dtype,bs,hp", STAGED, ids=[c[0] for c in STAGED])
+def test_pooled_step_resident_matches_oracle(name, dtype, bs, hp):
+    """Every page fits: the first step copies each page in once, later steps hit; the
+    host buffers, flushed after each step, follow the oracle's trajectory."""
+    n = 3 * 4096 + 1232 + (0 if name == "ademamix" else 5)
+    hp = dict(hp, blocksize=bs)
+    print(f"\n[case] pooled resident {name} {dtype} B{bs} n={n}", flush=True)
+    p0 = W.to_dtype(W.normal_f32([1770, 1], n, 0.02), dtype)
+    q = Quant8(hp, p0, dtype)
+    _page_out(q)
+    pool = bitopt.PagePool(hp, 4096, nframes=6)
+    cmp = Compare()
+    for t in range(1, 4):
+        g = W.normal_f32([1770, 2, t], n, 0.01)
+        if hp.get("skip_zeros"):
+            g[2048 * 2: 2048 * 5] = 0.0
+        g = W.to_dtype(g, dtype)
+        _pooled_step(pool, q, t, to_dev(g, dtype))
+        pool.flush()
+        q.step_oracle(t, g)
+        q.compare(cmp, f"step {t}")
+    st = pool.stats()
+    assert st == dict(resident=4, page_ins=4, write_backs=12, hits=8), st
+    pool.close()
+    print("  " + cmp.summary())
+
+
+@pytest.mark.parametrize("name,dtype,bs,hp", STAGED, ids=[c[0] for c in STAGED])
+def test_pooled_step_oversubscribed_equals_device_resident(name, dtype, bs, hp):
+    """Two tensors of six pages each through three frames (every step evicts and
+    writes back), one of them stepped on a second stream for a while, and an evicting
+    flush midway: bit-identical to the device-resident step over four steps."""
+    n = 5 * 4096 + 48
+    hp = dict(hp, blocksize=bs)
+    print(f"\n[case] pooled oversubscribed {name} {dtype} B{bs} n={n}", flush=True)
+    pool = bitopt.PagePool(hp, 4096, nframes=3)
+    side = torch.cuda.Stream()
+    pairs = []
+    for j in range(2):
+        p0 = W.to_dtype(W.normal_f32([1780, 1, j], n, 0.02), dtype)
+        A, B = Quant8(hp, p0, dtype), Quant8(hp, p0, dtype)
+        _page_out(A)
+        pairs.append((A, B))
+    for t in range(1, 5):
+        for j, (A, B) in enumerate(pairs):
+            g = W.normal_f32([1780, 2, t, j], n, 0.01)
+            if hp.get("skip_zeros"):
+                g[: n // 3] = 0.0
+            gd = to_dev(W.to_dtype(g, dtype), dtype)
+            if j == 1 and t in (2, 3):                     # the second tensor on another stream
+                side.wait_stream(torch.cuda.current_stream())
+                _pooled_step(pool, A, t, gd, stream=side)
+                torch.cuda.current_stream().wait_stream(side)
+            else:
+                _pooled_step(pool, A, t, gd)
+            B.step_gpu(t, gd)
+        pool.flush(evict=(t == 2))
+        torch.cuda.synchronize()
+        for j, (A, B) in enumerate(pairs):
+            for key in ("p", "s1", "s2", "a1", "a2"):
+                if A.d.get(key) is not None:
+                    np.testing.assert_array_equal(to_host(A.d[key]) if A.d[key].is_cuda else A.d[key].numpy(),
+                                                  to_host(B.d[key]), err_msg=f"step {t} tensor {j} {key}")
+    st = pool.stats()
+    assert st["page_ins"] == 4 * 2 * 6 and st["hits"] == 0, st
+    pool.close()
+
+
+def test_pooled_step_large_pages_and_refusals():
+    """Adam fp32 over 1 Mi-element pages, first with room for half the pages, then in a
+    pool that holds them all (no copies after the first step); the companion-buffer
+    and hyper-parameter checks of a pooled step."""
+    hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01, blocksize=256)
+    n = 5 * (1 << 20) + 3 * 4096 + 48
+    print(f"\n[case] pooled large adam f32 n={n}", flush=True)
+    p0 = W.normal_f32([1790, 1], n, 0.02)
+    A, B = Quant8(hp, p0, "f32"), Quant8(hp, p0, "f32")
+    _page_out(A)
+    small = bitopt.PagePool(hp, 1 << 20, nframes=3)
+    big = bitopt.PagePool(hp, 1 << 20, nframes=6)
+    for t in range(1, 6):
+        gd = to_dev(W.normal_f32([1790, 2, t], n, 0.01), "f32")
+        if t == 3:                                         # move the state from one pool to the other
+            small.flush(evict=True)
+        _pooled_step(small if t < 3 else big, A, t, gd)
+        B.step_gpu(t, gd)
+    big.flush()
+    torch.cuda.synchronize()
+    for key in ("p", "s1", "s2", "a1", "a2"):
+        np.testing.assert_array_equal(to_host(A.d[key]) if A.d[key].is_cuda else A.d[key].numpy(),
+                                      to_host(B.d[key]), err_msg=key)
+    assert big.stats()["page_ins"] == 6 and big.stats()["hits"] == 12, big.stats()
+    d = A.d
+    other = bitopt.host_state(A.nb, torch.float32)
+    with pytest.raises(bitopt.BitoptError, match="companion"):
+        big.step(hp, 6, d["p"], d["p"], d["s1"], other, d["q1"], d["s2"], d["a2"], d["q2"])
+    with pytest.raises(bitopt.BitoptError, match="blocksize"):
+        nb = -(-n // 2048)
+        big.step(dict(hp, blocksize=2048), 6, d["p"], d["p"], d["s1"], d["a1"][:nb], d["q1"], d["s2"], d["a2"][:nb],
+                 d["q2"])
+    small.close()
+    big.close()
+    torch.cuda.synchronize()
