@@ -55,8 +55,8 @@ def workload_by_name(name):
         "adamw_bf16_tensorwise": lambda: W.f3_tensorwise_4096("bf16"),
         "adamw_fp32_b256_paged": lambda: W.f4_paged_4096("f32"),
         "adamw_fp32_b256_staged": lambda: W.f4_staged_4096("f32"),
-        "adamw_fp32_b256_pooled": lambda: W.f4_pooled_4096("f32", 1 << 23, 2),
-        "adamw_fp32_b256_pooled_thrash": lambda: W.f4_pooled_4096("f32", 1 << 22, 2),
+        "adamw_fp32_b256_pooled": lambda: W.f4_pooled_4096("f32", 1 << 24, 2),
+        "adamw_fp32_b256_pooled_thrash": lambda: W.f4_pooled_4096("f32", 1 << 22, 3),
         "adam_fp32_256x256": W.c1_adam_256,
         "adam_fp32_1024x9": W.adam_small_1024x9,
         "adamw32_fp32_4096": lambda: W.adamw_32bit_4096("f32"),
@@ -577,11 +577,11 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_w
         step = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == kname]
         if not step:      # names spelled differently in the two outputs: any library kernel
             step = [float(r["Counter_Value"]) for r in rows if "bitopt::" in r["Kernel_Name"]]
-        # the calibration copy is the runtime's device-to-device blit kernel: the
-        # dispatches of it with the largest grid
-        blits = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        gmax = max(int(r["Grid_Size"]) for r in blits)
-        copy = [float(r["Counter_Value"]) for r in blits if int(r["Grid_Size"]) == gmax]
+        # the calibration copy is the runtime's device-to-device blit kernel, by far the
+        # largest blit of the run (paged workloads' host copies may use blit kernels too)
+        blits = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        vmax = max(blits)
+        copy = [v for v in blits if v >= 0.5 * vmax]
         return step, copy
 
     fs, fc = counter("FETCH_SIZE", "fetch")
@@ -602,6 +602,11 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_w
     if wl.hp.get("skip_zeros"):
         alg = skip_aware_bytes(wl, Replica(wl, 0, torch.device("cuda:0")).g, alg)
     kelems = sum(t.numel for t in wl.tensors)
+    unit = wl.extra.get("chunk") or wl.extra.get("page")
+    if unit and unit < kelems:
+        # staged or pooled state: one launch per chunk or page (4096x4096 splits evenly)
+        alg = alg * unit / kelems
+        kelems = unit
     extra = {}
     for gi, group in enumerate(counter_groups):
         rows = _csv_rows(os.path.join(outdir, f"counters{gi}"), "counter_collection.csv")

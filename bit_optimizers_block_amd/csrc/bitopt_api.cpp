@@ -99,9 +99,13 @@ bitopt::StepScalars make_scalars(const bitopt_hparams& h, int32_t t) {
     s.omb3 = (float)(1.0 - b3t);
     s.alpha_t = (float)alpha_at((double)h.alpha, t, h.t_alpha);
     s.max_unorm = h.max_unorm;
+    // the exact product of the two fp32 scalars, rounded once
+    s.lric1 = (float)((double)s.lr * (double)s.ic1);
     // the root optimizers' denominator then stays below 2^85, so its hardware
-    // reciprocal is a normal number (the error bound of the 16-bit parameter path)
-    s.fast_root = (h.eps <= 0x1p60f && s.rs2 <= 0x1p20f) ? 1 : 0;
+    // reciprocal is a normal number, and the folded numerator scale carries one
+    // rounding (the error bound of the 16-bit parameter path)
+    const bool lric1_ok = s.lric1 == 0.0f || (std::isfinite(s.lric1) && s.lric1 >= 0x1p-126f);
+    s.fast_root = (h.eps <= 0x1p60f && s.rs2 <= 0x1p20f && lric1_ok) ? 1 : 0;
     return s;
 }
 

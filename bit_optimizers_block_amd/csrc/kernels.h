@@ -42,7 +42,8 @@ struct StepScalars {
     float omb1, omb2, ic1, rs2, decay;
     float b3t, omb3, alpha_t;
     float max_unorm;
-    int32_t fast_root;   // eps <= 2^60 and rs2 <= 2^20 (see root_delta_estimate)
+    float lric1;         // fl(lr * ic1): the Adam step's numerator scale in the estimate path
+    int32_t fast_root;   // eps <= 2^60, rs2 <= 2^20, lric1 zero or normal (see root_delta_estimate)
 };
 
 // One tensor of a multi-tensor launch (device table entry): the same fields as a
@@ -490,20 +491,25 @@ __device__ __forceinline__ float root_delta(const StepScalars& s, float p, float
 
 // The same parameter step from the hardware estimates: square root and reciprocal
 // each within one ulp (for v outside (0, 2^-96) and a denominator below 2^85, which
-// eps <= 2^60 and rs2 <= 2^20 ensure), so the step differs from root_delta by at most
-// 13 units of 2^-24 relative, plus 2^-140 absolute where it is subnormal.
+// eps <= 2^60 and rs2 <= 2^20 ensure).  The denominator is one fused multiply-add;
+// Adam scales m once by fl(lr * ic1) (zero or normal) instead of by ic1 and then lr.
+// Against root_delta's roundings this leaves the step within 14 units of 2^-24
+// relative (Adam: 8 units from the exact quotient here, 6 there; AdEMAMix and the
+// others fewer), plus 2^-140 absolute where it is subnormal.
 template <int OPT>
 __device__ __forceinline__ float root_delta_estimate(const StepScalars& s, float p, float g, const float st[3]) {
     const float r = __builtin_amdgcn_sqrtf(st[RootState<OPT>::v]);
+    if constexpr (OPT == kAdam) {
+        const float den = __builtin_fmaf(r, s.rs2, s.eps);
+        const float num = st[0] * s.lric1;
+        return num * __builtin_amdgcn_rcpf(den);
+    }
     float num, den;
-    if constexpr (OPT == kAdam || OPT == kAdemamix) {
-        den = r * s.rs2;
-        den = den + s.eps;
+    if constexpr (OPT == kAdemamix) {
+        den = __builtin_fmaf(r, s.rs2, s.eps);
         num = st[0] * s.ic1;
-        if constexpr (OPT == kAdemamix) {
-            const float t2 = s.alpha_t * st[1];
-            num = num + t2;
-        }
+        const float t2 = s.alpha_t * st[1];
+        num = num + t2;
     } else {
         const float t1 = s.wd * p;
         num = g + t1;
@@ -513,22 +519,34 @@ __device__ __forceinline__ float root_delta_estimate(const StepScalars& s, float
     return s.lr * u;
 }
 
-// Whether the new 16-bit parameter formed from an estimated step d, z = fl(pd - d),
-// rounds to the same 16-bit value as the one formed from the exact step dx: true when
-// fl(pd - (d + e)) and fl(pd - (d - e)) round alike, e = |d| 2^-19 + 2^-120 being more
-// than twice the distance of d from dx (13 * 2^-24 |d| + 2^-140), so that the rounded
-// sums d + e and d - e still bracket dx.  The correctly rounded subtraction and the
-// 16-bit rounding are both monotone, so fl(pd - dx) -- and z -- lie between the two
-// bounds and round alike.  A non-finite margin (d not finite) makes the test fail.
+// The new 16-bit parameters of a quad from estimated steps d[i], when the estimate
+// provably gives the exact path's bits: with e = |d| 2^-19 + 2^-120 -- more than the
+// distance of d from the exact step dx (14 * 2^-24 |d| + 2^-140) plus the rounding of
+// d +- e, so that the rounded sums d + e and d - e still bracket dx -- the bounds
+// lo = fl(pd - (d + e)) and hi = fl(pd - (d - e)) enclose fl(pd - dx) (correctly
+// rounded subtraction is monotone); when lo and hi round to the same 16-bit value, so
+// does fl(pd - dx), the exact path's parameter.  The quad's lo values, rounded and
+// packed two per word, are then the result (w[0], w[1]), and the function returns
+// true; it returns false when any element's bounds round apart or any margin is not
+// finite (a step that is NaN or infinite).
 template <int DT>
-__device__ __forceinline__ bool rounds_alike(float pd, float d) {
-    const float e = __builtin_fmaf(__builtin_fabsf(d), 0x1p-19f, 0x1p-120f);
-    const float dhi = d + e;
-    const float dlo = d - e;
-    const float lo = pd - dhi;
-    const float hi = pd - dlo;
-    const uint32_t w = narrow2<DT>(lo, hi);
-    return (w & 0xffffu) == (w >> 16) && e < __builtin_inff();
+__device__ __forceinline__ bool quad_rounds_alike(const float (&pd)[4], const float (&d)[4], uint32_t (&w)[2]) {
+    float lo[4], hi[4];
+    uint32_t emax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_fmaf(__builtin_fabsf(d[i]), 0x1p-19f, 0x1p-120f);
+        const float dhi = d[i] + e;
+        const float dlo = d[i] - e;
+        lo[i] = pd[i] - dhi;
+        hi[i] = pd[i] - dlo;
+        emax = max(emax, __float_as_uint(e));      // e >= 0: bits order as values; NaN above +inf
+    }
+    w[0] = narrow2<DT>(lo[0], lo[1]);
+    w[1] = narrow2<DT>(lo[2], lo[3]);
+    const uint32_t h0 = narrow2<DT>(hi[0], hi[1]);
+    const uint32_t h1 = narrow2<DT>(hi[2], hi[3]);
+    return w[0] == h0 && w[1] == h1 && emax < 0x7F800000u;
 }
 
 // One element of one step.  st[] holds the decoded states on entry and the new
@@ -975,7 +993,9 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
 #pragma unroll
             for (int k = 0; k < NS; ++k) st[k][q][i] = live[q][i] ? s3[k] : st[k][q][i];
         }
-        bool applied = false;      // uniform: pf[q] already holds the new parameters
+        bool applied = false;      // uniform: the new parameters are formed (in pf[q] or pw)
+        bool packed = false;       // uniform: they are in pw, already rounded and packed
+        uint32_t pw[2] = {0u, 0u};
         if constexpr (ROOT) {
             // The unscaled square root is exact unless a second moment of the quad lies
             // in (0, 2^-96); then the quad takes the general one (same bits either way).
@@ -986,21 +1006,18 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
                 // within the estimate's bound changes its 16-bit rounding; the quad
                 // otherwise recomputes the step exactly (the same bits either way).
                 if (a.s.fast_root && !any_tiny) {
-                    float z[4];
-                    bool unsure = false;
+                    float d[4], pd[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
                                              NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
-                        const float d = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
-                        const float pd = decayed<OPT>(a.s, pf[q][i]);
-                        z[i] = pd - d;
-                        unsure |= !rounds_alike<DT>(pd, d);
+                        d[i] = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
+                        pd[i] = decayed<OPT>(a.s, pf[q][i]);
                     }
-                    if (!wave_any(unsure)) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) pf[q][i] = z[i];
+                    const bool sure = quad_rounds_alike<DT>(pd, d, pw);
+                    if (!wave_any(!sure)) {
                         applied = true;
+                        packed = true;
                     }
                 }
             }
@@ -1019,11 +1036,22 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
             }
         }
         if constexpr (EARLY) {
-            if (!applied) {
+            if (packed) {
+                if constexpr (DT != kF32) {
+                    using Raw4 = typename Elem<DT>::Raw4;
+                    Raw4 r;
+                    r.x = pw[0];
+                    r.y = pw[1];
+                    st_stream(r, reinterpret_cast<Raw4*>(reinterpret_cast<typename Elem<DT>::T*>(a.p) +
+                                                         L::elem(base, lane, q)));
+                }
+            } else {
+                if (!applied) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pf[q][i] = apply_step<OPT>(a.s, pf[q][i], dl[q][i]);
+                    for (int i = 0; i < 4; ++i) pf[q][i] = apply_step<OPT>(a.s, pf[q][i], dl[q][i]);
+                }
+                store4<DT>(a.p, L::elem(base, lane, q), pf[q]);
             }
-            store4<DT>(a.p, L::elem(base, lane, q), pf[q]);
         }
     }
 
