@@ -519,34 +519,38 @@ __device__ __forceinline__ float root_delta_estimate(const StepScalars& s, float
     return s.lr * u;
 }
 
-// The new 16-bit parameters of a quad from estimated steps d[i], when the estimate
-// provably gives the exact path's bits: with e = |d| 2^-19 + 2^-120 -- more than the
-// distance of d from the exact step dx (14 * 2^-24 |d| + 2^-140) plus the rounding of
-// d +- e, so that the rounded sums d + e and d - e still bracket dx -- the bounds
-// lo = fl(pd - (d + e)) and hi = fl(pd - (d - e)) enclose fl(pd - dx) (correctly
-// rounded subtraction is monotone); when lo and hi round to the same 16-bit value, so
-// does fl(pd - dx), the exact path's parameter.  The quad's lo values, rounded and
-// packed two per word, are then the result (w[0], w[1]), and the function returns
-// true; it returns false when any element's bounds round apart or any margin is not
-// finite (a step that is NaN or infinite).
+// New 16-bit parameters from estimated steps, two elements at a time, when the
+// estimate provably gives the exact path's bits: with e = |d| 2^-19 + 2^-120 -- more
+// than the distance of d from the exact step dx (14 * 2^-24 |d| + 2^-140) plus the
+// rounding of d +- e, so that the rounded sums d + e and d - e still bracket dx --
+// the bounds lo = fl(pd - (d + e)) and hi = fl(pd - (d - e)) enclose fl(pd - dx)
+// (correctly rounded subtraction is monotone); when lo and hi round to the same
+// 16-bit value, so does fl(pd - dx), the exact path's parameter.  w receives the two
+// lo values rounded and packed; the result is whether both pairs of bounds round
+// alike.  emax accumulates the margins' bit patterns (e >= 0, so they order as
+// values, and NaN lies above +inf): the caller requires emax < +inf, which rejects a
+// step that is NaN or infinite.
+// The same test for one element, whose bounds are rounded in one pair: fl(pd - d) is
+// then the result (the form that keeps the fewest values live).
 template <int DT>
-__device__ __forceinline__ bool quad_rounds_alike(const float (&pd)[4], const float (&d)[4], uint32_t (&w)[2]) {
-    float lo[4], hi[4];
-    uint32_t emax = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_fmaf(__builtin_fabsf(d[i]), 0x1p-19f, 0x1p-120f);
-        const float dhi = d[i] + e;
-        const float dlo = d[i] - e;
-        lo[i] = pd[i] - dhi;
-        hi[i] = pd[i] - dlo;
-        emax = max(emax, __float_as_uint(e));      // e >= 0: bits order as values; NaN above +inf
-    }
-    w[0] = narrow2<DT>(lo[0], lo[1]);
-    w[1] = narrow2<DT>(lo[2], lo[3]);
-    const uint32_t h0 = narrow2<DT>(hi[0], hi[1]);
-    const uint32_t h1 = narrow2<DT>(hi[2], hi[3]);
-    return w[0] == h0 && w[1] == h1 && emax < 0x7F800000u;
+__device__ __forceinline__ bool rounds_alike(float pd, float d) {
+    const float e = __builtin_fmaf(__builtin_fabsf(d), 0x1p-19f, 0x1p-120f);
+    const float dhi = d + e;
+    const float dlo = d - e;
+    const uint32_t w = narrow2<DT>(pd - dhi, pd - dlo);
+    return (w & 0xffffu) == (w >> 16) && e < __builtin_inff();
+}
+
+template <int DT>
+__device__ __forceinline__ bool pair_rounds_alike(float pd0, float d0, float pd1, float d1, uint32_t& w,
+                                                  uint32_t& emax) {
+    const float e0 = __builtin_fmaf(__builtin_fabsf(d0), 0x1p-19f, 0x1p-120f);
+    const float e1 = __builtin_fmaf(__builtin_fabsf(d1), 0x1p-19f, 0x1p-120f);
+    const float dhi0 = d0 + e0, dlo0 = d0 - e0;
+    const float dhi1 = d1 + e1, dlo1 = d1 - e1;
+    emax = max(emax, max(__float_as_uint(e0), __float_as_uint(e1)));
+    w = narrow2<DT>(pd0 - dhi0, pd1 - dhi1);
+    return w == narrow2<DT>(pd0 - dlo0, pd1 - dlo1);
 }
 
 // One element of one step.  st[] holds the decoded states on entry and the new
@@ -1005,16 +1009,41 @@ __device__ __forceinline__ void process_tile(const StepArgs& a, const MapLDS& M1
                 // stored parameter whenever the rounding test shows that no error
                 // within the estimate's bound changes its 16-bit rounding; the quad
                 // otherwise recomputes the step exactly (the same bits either way).
-                if (a.s.fast_root && !any_tiny) {
-                    float d[4], pd[4];
+                if (OPT == kAdemamix && a.s.fast_root && !any_tiny) {
+                    // three states: per element, the form with the fewest live values
+                    float z[4];
+                    bool unsure = false;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
                                              NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
-                        d[i] = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
-                        pd[i] = decayed<OPT>(a.s, pf[q][i]);
+                        const float d = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
+                        const float pd = decayed<OPT>(a.s, pf[q][i]);
+                        z[i] = pd - d;
+                        unsure |= !rounds_alike<DT>(pd, d);
                     }
-                    const bool sure = quad_rounds_alike<DT>(pd, d, pw);
+                    if (!wave_any(unsure)) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pf[q][i] = z[i];
+                        applied = true;
+                    }
+                } else if (a.s.fast_root && !any_tiny) {
+                    bool sure = true;
+                    uint32_t emax = 0;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        float d[2], pd[2];
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const int i = 2 * h + j;
+                            const float s3[3] = {st[0][q][i], NS > 1 ? st[NS > 1 ? 1 : 0][q][i] : 0.0f,
+                                                 NS > 2 ? st[NS > 2 ? 2 : 0][q][i] : 0.0f};
+                            d[j] = root_delta_estimate<OPT>(a.s, pf[q][i], gq[i], s3);
+                            pd[j] = decayed<OPT>(a.s, pf[q][i]);
+                        }
+                        sure = pair_rounds_alike<DT>(pd[0], d[0], pd[1], d[1], pw[h], emax) && sure;
+                    }
+                    sure = sure && emax < 0x7F800000u;
                     if (!wave_any(!sure)) {
                         applied = true;
                         packed = true;
