@@ -132,6 +132,9 @@ def lib():
             "bitopt_multi_plan_build": ([HP, ctypes.POINTER(Tensor), i32, P, i64, ctypes.POINTER(MultiPlanC), P],
                                         ctypes.c_int),
             "bitopt_step_multi_planned": ([ctypes.POINTER(MultiPlanC), HP, i32, P, P, P], ctypes.c_int),
+            "bitopt_device_scalars_bytes": ([], i64),
+            "bitopt_device_scalars_write": ([HP, i32, P, i64], ctypes.c_int),
+            "bitopt_step_multi_planned_dscalars": ([ctypes.POINTER(MultiPlanC), HP, P, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -502,6 +505,30 @@ class MultiPlan:
         h = make_hparams(hp)
         _check(lib().bitopt_step_multi_planned(ctypes.byref(self.c), ctypes.byref(h), int(step), _ptr(qmap1),
                                                _ptr(qmap2), _stream(stream)))
+
+    def step_dscalars(self, hp, scalars, qmap1=None, qmap2=None, stream=None):
+        """The planned step with its per-step scalars read from `scalars` (a device
+        uint8 tensor of device_scalars_bytes() bytes, see device_scalars) when the
+        kernels run: a captured graph of this call steps with the buffer's contents
+        at each replay."""
+        h = make_hparams(hp)
+        _need(scalars, "scalars", torch.uint8)
+        if scalars.numel() < device_scalars_bytes():
+            raise ValueError("scalars is too small")
+        _check(lib().bitopt_step_multi_planned_dscalars(ctypes.byref(self.c), ctypes.byref(h), _ptr(scalars),
+                                                        _ptr(qmap1), _ptr(qmap2), _stream(stream)))
+
+
+def device_scalars_bytes() -> int:
+    return int(lib().bitopt_device_scalars_bytes())
+
+
+def device_scalars(hp, step) -> torch.Tensor:
+    """The per-step scalars of (hp, step) in the kernels' device layout, as a CPU uint8
+    tensor (copy it into the device buffer that step_dscalars reads)."""
+    out = torch.empty(device_scalars_bytes(), dtype=torch.uint8)
+    _check(lib().bitopt_device_scalars_write(ctypes.byref(make_hparams(hp)), int(step), _ptr(out), out.numel()))
+    return out
 
 
 def step_multi(hp, step, tensors, qmap1=None, qmap2=None, workspace=None, stream=None):

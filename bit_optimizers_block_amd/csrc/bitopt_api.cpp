@@ -969,11 +969,14 @@ int bitopt_multi_plan_build(const bitopt_hparams* hp, const bitopt_tensor* tenso
     return ok();
 }
 
-int bitopt_step_multi_planned(const bitopt_multi_plan* plan, const bitopt_hparams* hp, int32_t step,
-                              const float* qmap1, const float* qmap2, void* stream) {
-    const char* fn = "bitopt_step_multi_planned";
+}  // extern "C"
+
+namespace {
+
+// The launches of a planned step; sdev: device scalars (or NULL: sc by value).
+int run_planned(const bitopt_multi_plan* plan, const bitopt_hparams* hp, const bitopt::StepScalars& sc,
+                const void* sdev, const float* qmap1, const float* qmap2, void* stream, const char* fn) {
     if (!plan) return fail(BITOPT_ERR_INVALID_ARG, "%s: plan is NULL", fn);
-    if (int rc = check_hparams(hp, step, 0, fn)) return rc;
     if (hp->optimizer != plan->optimizer || hp->blocksize != plan->blocksize)
         return fail(BITOPT_ERR_INVALID_ARG, "%s: the plan was built for optimizer %d, blocksize %d", fn,
                     plan->optimizer, plan->blocksize);
@@ -984,11 +987,11 @@ int bitopt_step_multi_planned(const bitopt_multi_plan* plan, const bitopt_hparam
     for (int32_t i = 0; i < plan->nlaunch; ++i) any8 = any8 || plan->launch[i].kind8;
     if (any8 && (!qmap1 || (two && !qmap2))) return fail(BITOPT_ERR_INVALID_ARG, "%s: NULL qmap", fn);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const bitopt::StepScalars sc = make_scalars(*hp, step);
     for (int32_t i = 0; i < plan->nlaunch; ++i) {
         const bitopt_multi_launch& L = plan->launch[i];
         bitopt::StepArgs a{};
         a.q1 = qmap1; a.q2 = qmap2; a.s = sc;
+        a.sdev = static_cast<const bitopt::StepScalars*>(sdev);
         a.table = reinterpret_cast<const bitopt::TensorDesc*>(plan->workspace) + L.first;
         a.ntab = L.count;
         a.total_tiles = L.tiles;
@@ -998,6 +1001,40 @@ int bitopt_step_multi_planned(const bitopt_multi_plan* plan, const bitopt_hparam
         if (e != hipSuccess) return device_status(e, fn);
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitopt_step_multi_planned(const bitopt_multi_plan* plan, const bitopt_hparams* hp, int32_t step,
+                              const float* qmap1, const float* qmap2, void* stream) {
+    const char* fn = "bitopt_step_multi_planned";
+    if (int rc = check_hparams(hp, step, 0, fn)) return rc;
+    return run_planned(plan, hp, make_scalars(*hp, step), nullptr, qmap1, qmap2, stream, fn);
+}
+
+int64_t bitopt_device_scalars_bytes(void) { return (int64_t)sizeof(bitopt::StepScalars); }
+
+int bitopt_device_scalars_write(const bitopt_hparams* hp, int32_t step, void* out, int64_t out_bytes) {
+    const char* fn = "bitopt_device_scalars_write";
+    if (int rc = check_hparams(hp, step, 0, fn)) return rc;
+    if (!out) return fail(BITOPT_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (out_bytes < (int64_t)sizeof(bitopt::StepScalars))
+        return fail(BITOPT_ERR_INVALID_ARG, "%s: out holds %lld bytes, %lld needed", fn, (long long)out_bytes,
+                    (long long)sizeof(bitopt::StepScalars));
+    const bitopt::StepScalars sc = make_scalars(*hp, step);
+    std::memcpy(out, &sc, sizeof sc);
+    return ok();
+}
+
+int bitopt_step_multi_planned_dscalars(const bitopt_multi_plan* plan, const bitopt_hparams* hp, const void* scalars,
+                                       const float* qmap1, const float* qmap2, void* stream) {
+    const char* fn = "bitopt_step_multi_planned_dscalars";
+    if (int rc = check_hparams(hp, 1, 0, fn)) return rc;
+    if (!scalars) return fail(BITOPT_ERR_INVALID_ARG, "%s: scalars is NULL", fn);
+    if (!aligned(scalars, 16)) return fail(BITOPT_ERR_INVALID_ARG, "%s: scalars not 16-byte aligned", fn);
+    return run_planned(plan, hp, bitopt::StepScalars{}, scalars, qmap1, qmap2, stream, fn);
 }
 
 int bitopt_step_multi(const bitopt_hparams* hp, int32_t step, const bitopt_tensor* tensors, int32_t count,

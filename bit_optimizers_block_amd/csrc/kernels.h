@@ -82,6 +82,7 @@ struct StepArgs {
     int64_t total_tiles;
     uint32_t* ws;              // tensor-wide step: workspace shared by its passes
     int32_t parts;             // tensor-wide step: groups of pass 1 (partial results in ws)
+    const StepScalars* sdev;   // multi-tensor launch: scalars read from device memory (else s)
 };
 
 template <int OPT> struct NumStates { static constexpr int v = OPT == kAdemamix ? 3 : (OPT == kAdam ? 2 : 1); };
@@ -1632,6 +1633,8 @@ void k_step(StepArgs a) {
         return;
     }
     if constexpr (MULTI) {
+        // scalars the caller writes into device memory before each launch or graph replay
+        if (a.sdev) a.s = *a.sdev;      // uniform
         const BITOPT_CONSTANT TensorDesc* tab = (const BITOPT_CONSTANT TensorDesc*)a.table;
         for (int i = threadIdx.x; i < a.ntab; i += kThreads) T0[i] = (uint32_t)tab[i].tile0;
         __syncthreads();

@@ -29,7 +29,8 @@
  *   - Any alignment is accepted; buffers aligned to 16 bytes take the vector path.
  *   - Step calls form their per-step scalars on the host when called and pass them
  *     as kernel arguments: a step captured into a HIP graph replays the step number
- *     (bias corrections, AdEMAMix schedules) it was captured with.
+ *     (bias corrections, AdEMAMix schedules) it was captured with.  The exception is
+ *     bitopt_step_multi_planned_dscalars, whose kernels read them from device memory.
  *   - Calls are stateless and re-entrant.  Fresh state buffers are zero-filled:
  *     codes 0 and absmax 0 decode to zero.
  *   - Element arithmetic is IEEE fp32 (no contraction to FMA, correctly rounded
@@ -449,11 +450,35 @@ BITOPT_API int bitopt_multi_plan_build(const bitopt_hparams* hp, const bitopt_te
  * Graph capture: the per-step scalars (bias corrections, schedules) are formed on
  * the host from hp and step when the call is made and passed as kernel arguments,
  * so a captured call replays the step number and hyper-parameters it was captured
- * with; capture one graph per step value, or call eagerly.  (The same holds for every
- * step entry point.)
+ * with; capture one graph per step value, call eagerly, or use the device-scalar form
+ * below.  (The same holds for every other step entry point.)
  */
 BITOPT_API int bitopt_step_multi_planned(const bitopt_multi_plan* plan, const bitopt_hparams* hp, int32_t step,
                                          const float* qmap1, const float* qmap2, void* stream);
+
+/*
+ * The per-step scalars in device form: bitopt_device_scalars_bytes() bytes (at most
+ * 64) that bitopt_device_scalars_write fills, on the host, for (hp, step) -- the bias
+ * corrections of the optimizer pages' update rules and the AdEMAMix schedules, as the
+ * other entry points form them.  out: host memory of out_bytes bytes.
+ */
+BITOPT_API int64_t bitopt_device_scalars_bytes(void);
+BITOPT_API int bitopt_device_scalars_write(const bitopt_hparams* hp, int32_t step, void* out, int64_t out_bytes);
+
+/*
+ * A planned step whose kernels read the per-step scalars from device memory:
+ * `scalars` (device, 16-byte aligned, bitopt_device_scalars_bytes() bytes, written by
+ * the caller from bitopt_device_scalars_write with this hp, e.g. by a copy on `stream`)
+ * is read when the kernels run, so a graph that captures this call steps with whatever
+ * the buffer holds at each replay: update it before each replay (a training loop: write
+ * step t's scalars, copy them in, replay).  hp selects the kernels (optimizer, blocksize,
+ * skip_zeros, whether max_unorm > 0) and must equal the hp the scalars were written
+ * with in those fields.  The results equal bitopt_step_multi_planned's for that step.
+ * Errors: as bitopt_step_multi_planned; NULL or misaligned scalars give INVALID_ARG.
+ */
+BITOPT_API int bitopt_step_multi_planned_dscalars(const bitopt_multi_plan* plan, const bitopt_hparams* hp,
+                                                  const void* scalars, const float* qmap1, const float* qmap2,
+                                                  void* stream);
 
 /*
  * Plan and step in one call: bitopt_multi_plan_build followed by

@@ -249,3 +249,40 @@ def test_page_pool_argument_errors(B):
     assert L.bitopt_page_pool_flush(None, 0, None) == E
     assert L.bitopt_page_pool_stats(None, (ctypes.c_int64 * 4)()) == E
     assert L.bitopt_page_pool_destroy(None) == B.OK
+
+
+def test_device_scalars_layout_and_errors(B):
+    """The device-form scalars hold the 14 host scalars first, in the order
+    bitopt_step_scalars gives them (the kernels' struct); argument checks of the
+    device-scalar planned step (no launch)."""
+    L = B.lib()
+    E = B.ERR_INVALID_ARG
+    nbytes = L.bitopt_device_scalars_bytes()
+    assert 14 * 4 <= nbytes <= 64
+    for hp in (dict(optimizer="adam", lr=1e-3, weight_decay=0.01), dict(optimizer="ademamix", t_alpha=5, t_beta3=5,
+                                                                       alpha=5.0)):
+        h = B.make_hparams(hp)
+        for t in (1, 3, 1000):
+            out = (ctypes.c_uint8 * nbytes)()
+            assert L.bitopt_device_scalars_write(ctypes.byref(h), t, out, nbytes) == B.OK
+            host = (ctypes.c_float * 14)()
+            assert L.bitopt_step_scalars(ctypes.byref(h), t, host) == B.OK
+            got = np.frombuffer(bytes(out), np.float32)[:14]
+            np.testing.assert_array_equal(got.view(np.uint32), np.frombuffer(bytes(host), np.uint32))
+    h = B.make_hparams(dict(optimizer="adam"))
+    out = (ctypes.c_uint8 * nbytes)()
+    assert L.bitopt_device_scalars_write(ctypes.byref(h), 1, out, nbytes - 1) == E
+    assert L.bitopt_device_scalars_write(ctypes.byref(h), 0, out, nbytes) == E
+    assert L.bitopt_device_scalars_write(ctypes.byref(h), 1, None, nbytes) == E
+    empty = B.MultiPlanC()
+    arr = (B.Tensor * 1)()
+    P = ctypes.c_void_p(16)
+    assert L.bitopt_multi_plan_build(ctypes.byref(h), arr, 0, P, 0, ctypes.byref(empty), None) == B.OK
+    S = ctypes.c_void_p(256)
+    assert L.bitopt_step_multi_planned_dscalars(ctypes.byref(empty), ctypes.byref(h), S, None, None, None) == B.OK
+    assert L.bitopt_step_multi_planned_dscalars(ctypes.byref(empty), ctypes.byref(h), None, None, None, None) == E
+    assert L.bitopt_step_multi_planned_dscalars(ctypes.byref(empty), ctypes.byref(h), ctypes.c_void_p(260), None,
+                                                None, None) == E
+    h2 = B.make_hparams(dict(optimizer="momentum"))
+    assert L.bitopt_step_multi_planned_dscalars(ctypes.byref(empty), ctypes.byref(h2), S, None, None, None) == E
+    assert L.bitopt_step_multi_planned_dscalars(None, ctypes.byref(h), S, None, None, None) == E

@@ -123,3 +123,60 @@ def test_captured_multi_plan_step_replays_like_eager():
                 for key in ("p", "state1", "state2", "absmax1", "absmax2"):
                     if ta[key] is not None:
                         np.testing.assert_array_equal(to_host(ta[key]), to_host(tb[key]), err_msg=f"round {rnd} t {t} {key}")
+
+
+@pytest.mark.parametrize("opt", ["adam", "ademamix"])
+def test_captured_device_scalar_step_follows_the_step_number(opt):
+    """bitopt_step_multi_planned_dscalars reads the per-step scalars from device memory:
+    ONE captured graph, its scalar buffer rewritten before each replay with step t's
+    values (bias corrections; AdEMAMix's alpha and beta3 schedules), steps t = 1..5
+    exactly as the eager planned step at t = 1..5 on a twin set of tensors."""
+    if opt == "adam":
+        hp = dict(optimizer="adam", lr=1e-3, weight_decay=0.01, blocksize=256)
+    else:
+        hp = dict(optimizer="ademamix", lr=1e-3, beta3=0.9999, alpha=5.0, t_alpha=4, t_beta3=4, blocksize=256)
+    k = 2 if opt == "ademamix" else 1
+    specs = [(5000, "f32", True), (4096, "bf16", True), (3008, "f16", True), (2048, "f32", False)]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    q1, q2 = bitopt.create_dynamic_map(True).cuda(), bitopt.create_dynamic_map(False).cuda()
+    print(f"\n[case] device-scalar graph replay {opt}", flush=True)
+
+    def make():
+        ts = []
+        for i, (n, dt, eight) in enumerate(specs):
+            nb = (n + 255) // 256
+            sd = torch.uint8 if eight else torch.float32
+            ts.append(dict(p=to_dev(W.to_dtype(W.normal_f32([1910, 1, i], n, 0.02), dt), dt),
+                           g=to_dev(W.to_dtype(W.normal_f32([1910, 2, i], n, 0.01), dt), dt),
+                           state1=torch.zeros(k * n, dtype=sd, device="cuda"),
+                           state2=torch.zeros(n, dtype=sd, device="cuda"),
+                           absmax1=torch.zeros(k * nb, device="cuda") if eight else None,
+                           absmax2=torch.zeros(nb, device="cuda") if eight else None, is_8bit=eight))
+        return ts
+
+    A, B = make(), make()
+    pa, pb = bitopt.MultiPlan(hp, A), bitopt.MultiPlan(hp, B)
+    scal = torch.zeros(bitopt.device_scalars_bytes(), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up on a scratch copy, as torch.cuda.graph expects
+        C = make()
+        scal.copy_(bitopt.device_scalars(hp, 1))
+        bitopt.MultiPlan(hp, C).step_dscalars(hp, scal, q1, q2)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.step_dscalars(hp, scal, q1, q2)
+    torch.cuda.synchronize()
+    for t in range(1, 6):
+        scal.copy_(bitopt.device_scalars(hp, t))
+        g.replay()
+        pb.step(hp, t, q1, q2)
+        scratch = torch.randn(1 << 18, device="cuda").sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        for ta, tb in zip(A, B):
+            for key in ("p", "state1", "state2", "absmax1", "absmax2"):
+                if ta[key] is not None:
+                    np.testing.assert_array_equal(to_host(ta[key]), to_host(tb[key]), err_msg=f"t {t} {key}")
