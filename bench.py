@@ -103,6 +103,18 @@ def workload_bytes(wl) -> float:
     return total
 
 
+def replica_grad(wl, r):
+    """The fp32 gradient of replica r of a single-tensor workload (rows zeroed for the
+    skip_zeros workloads)."""
+    t = wl.tensors[0]
+    g = W.normal_f32([wl.seed, 2, 0, r], t.numel, wl.g_scale)
+    if wl.zero_row_frac:
+        rows = t.shape[0]
+        mask = W.zero_row_mask([wl.seed, 3, 0, r], rows, wl.zero_row_frac)
+        g.reshape(rows, -1)[mask] = 0.0
+    return g
+
+
 def skip_aware_bytes(wl, g_dev, full_bytes):
     """With skip_zeros, a block whose gradients are all zero needs only its gradient
     read: the algorithmic bytes of a step over gradient g."""
@@ -234,11 +246,7 @@ class Replica:
         self.two = hp["optimizer"] in ("adam", "adamw", "ademamix")
         self.ws = torch.empty(bitopt.tensorwise_workspace_bytes(), dtype=torch.uint8, device=dev)
         p = W.normal_f32([wl.seed, 1, 0, r], n, wl.p_scale)
-        g = W.normal_f32([wl.seed, 2, 0, r], n, wl.g_scale)
-        if wl.zero_row_frac:
-            rows = t.shape[0]
-            mask = W.zero_row_mask([wl.seed, 3, 0, r], rows, wl.zero_row_frac)
-            g.reshape(rows, -1)[mask] = 0.0
+        g = replica_grad(wl, r)
         self.p = torch.from_numpy(p).to(dev).to(dt)
         self.g = torch.from_numpy(g).to(dev).to(dt)
         self.staged = wl.extra.get("paged") == "staged"
@@ -564,13 +572,42 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_w
     base_nc = ["--workload", workload, "--steps", str(steps), "--warmup", str(counter_warmup), "--no-cpu-baseline"]
     for gi, group in enumerate(counter_groups):
         cmds[f"counters{gi}"] = _rocprof(base_nc, os.path.join(outdir, f"counters{gi}"), ["--pmc", *group], env)
+    run = {"workload": workload, "source_hash": source_hash(), "commands": cmds, "traced_bench": tb,
+           "steps": steps, "counter_groups": [list(g) for g in counter_groups], "counter_warmup": counter_warmup}
+    with open(os.path.join(outdir, "run.json"), "w") as f:
+        json.dump(run, f, indent=1)
+    summarize_profile(workload, outdir)
 
+
+# FETCH_SIZE and WRITE_SIZE per KiB copied, as the 256 MiB calibration copy reads them
+# in the profiled runs (FETCH_SIZE counts half of the bytes read on this part).
+NOMINAL_SCALE = (2.0, 1.0)
+
+
+def summarize_profile(workload: str, outdir: str):
+    """The <workload>.md / .json summaries from the raw output of profile() in outdir
+    (its run.json records the commands, the traced run's benchmark line and the
+    library source hash at the time of the run)."""
+    outdir = os.path.abspath(outdir)
+    with open(os.path.join(outdir, "run.json")) as f:
+        run = json.load(f)
+    cmds, tb, steps = run["commands"], run["traced_bench"] or {}, run["steps"]
+    counter_groups, counter_warmup = run["counter_groups"], run["counter_warmup"]
     stats = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")]
     # the dominant library kernel (a multi-tensor step launches one kernel per tensor kind)
     step_stats = sorted((r for r in stats if "bitopt::" in r["Name"]), key=lambda r: -float(r["TotalDurationNs"]))
     kname = step_stats[0]["Name"]
     avg_ns = float(step_stats[0]["AverageNs"])
     calls = int(step_stats[0]["Calls"])
+    # the same kernel over the traced run's timed launches only (its last ones), the
+    # figure comparable with that run's time per step
+    trace = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_trace.csv") if r["Kernel_Name"] == kname]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace]
+    t_steps, t_warm = int(tb.get("steps") or 0), int(tb.get("warmup") or 0)
+    per_step = max(1, round(len(dur) / (t_steps + t_warm))) if t_steps + t_warm else 1
+    timed = dur[-per_step * t_steps:] if t_steps and dur else dur
+    timed_ns = sum(timed) / len(timed) if timed else avg_ns
 
     def counter(name, sub):
         rows = [r for r in _csv_rows(os.path.join(outdir, sub), "counter_collection.csv") if r["Counter_Name"] == name]
@@ -600,7 +637,8 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_w
         wl = W.Workload(**{**wl.__dict__, "tensors": [t for t in wl.tensors if t.eightbit == quant]})
     alg = workload_bytes(wl)
     if wl.hp.get("skip_zeros"):
-        alg = skip_aware_bytes(wl, Replica(wl, 0, torch.device("cuda:0")).g, alg)
+        # block liveness: the zeroed rows (no N(0, 1e-2) sample rounds to zero in 16 bits)
+        alg = skip_aware_bytes(wl, torch.from_numpy(replica_grad(wl, 0)), alg)
     kelems = sum(t.numel for t in wl.tensors)
     unit = wl.extra.get("chunk") or wl.extra.get("page")
     if unit and unit < kelems:
@@ -622,8 +660,10 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_w
             vals = [per[k] for k in sorted(per, key=lambda k: int(k) if k.isdigit() else 0)][-steps:]
             if vals:
                 extra[name] = sum(vals) / len(vals)
-    d = {"workload": workload, "kernel": kname, "source_hash": source_hash(),
+    d = {"workload": workload, "kernel": kname, "source_hash": run["source_hash"],
          "kernel_trace_calls": calls, "kernel_trace_avg_us": avg_ns / 1e3,
+         "kernel_timed_launches": len(timed), "kernel_timed_avg_us": timed_ns / 1e3,
+         "kernel_launches_per_step": per_step,
          "fetch_kib_per_launch": sum(fs) / len(fs), "write_kib_per_launch": sum(ws) / len(ws),
          "copy_calibration": {"bytes_each_way": COPY_ELEMS * 4, "fetch_kib": sum(fc) / len(fc),
                               "write_kib": sum(wc) / len(wc), "fetch_scale": f_scale, "write_scale": w_scale},
@@ -639,19 +679,27 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_w
         f.write(f"Kernel: `{kname}`\n\n")
         f.write("| figure | value |\n|---|---|\n")
         f.write(f"| kernel-trace calls | {calls} |\n")
-        f.write(f"| kernel-trace average duration | {avg_ns / 1e3:.2f} us |\n")
+        f.write(f"| kernel-trace average duration, all calls (warm-up included) | {avg_ns / 1e3:.2f} us |\n")
+        f.write(f"| kernel-trace average duration, the traced run's {len(timed)} timed launches "
+                f"({per_step} per step) | {timed_ns / 1e3:.2f} us |\n")
         if tb:
             f.write(f"| the traced run's own benchmark line: time per step (launch to launch) | "
                     f"{tb['ms_per_step'] * 1e3:.2f} us ({tb['value']} {tb['unit']}, {tb['roofline']['frac']} of peak) |\n")
         f.write(f"| algorithmic bytes per launch | {alg / 1e6:.1f} MB |\n")
-        f.write(f"| algorithmic GB/s at the trace average | {alg / avg_ns:.0f} |\n")
+        f.write(f"| algorithmic GB/s at the timed-launch average | {alg / timed_ns:.0f} "
+                f"({alg / timed_ns / HBM_PEAK_GBS:.4f} of the 8000 GB/s peak) |\n")
         f.write(f"| FETCH_SIZE per launch (raw) | {sum(fs) / len(fs):.0f} KiB |\n")
         f.write(f"| WRITE_SIZE per launch (raw) | {sum(ws) / len(ws):.0f} KiB |\n")
         f.write(f"| copy calibration (256 MiB each way): FETCH_SIZE / WRITE_SIZE | "
                 f"{sum(fc) / len(fc):.0f} / {sum(wc) / len(wc):.0f} KiB -> scale {f_scale:.4f} / {w_scale:.4f} |\n")
         f.write(f"| HBM traffic per launch (scaled) | {(fetch_b + write_b) / 1e6:.1f} MB "
                 f"({(fetch_b + write_b) / alg:.3f} x algorithmic) |\n")
-        f.write(f"| library source hash | {source_hash()} |\n\n")
+        if abs(f_scale / NOMINAL_SCALE[0] - 1.0) > 0.02 or abs(w_scale / NOMINAL_SCALE[1] - 1.0) > 0.02:
+            nb_ = (sum(fs) / len(fs) * NOMINAL_SCALE[0] + sum(ws) / len(ws) * NOMINAL_SCALE[1]) * 1024.0
+            f.write(f"| the same at the copy factors {NOMINAL_SCALE[0]:.1f} / {NOMINAL_SCALE[1]:.1f} that the "
+                    f"other runs measure (this run's copy counts read low) | {nb_ / 1e6:.1f} MB "
+                    f"({nb_ / alg:.3f} x algorithmic) |\n")
+        f.write(f"| library source hash | {run['source_hash']} |\n\n")
         if extra:
             f.write("| counter | per launch | per element (x64 for per-wave counts) |\n|---|---|---|\n")
             for name, v in extra.items():
@@ -664,7 +712,10 @@ def profile(workload: str, outdir: str, steps: int, counter_groups=(), counter_w
         f.write(f"Made by `python bench.py --profile <outdir> --workload {workload} --profile-steps {steps}{pc}` "
                 "(from the repository root), which runs the profiler passes below from /tmp with "
                 "TMPDIR=/tmp; raw output stays in the -d directories.  The trace pass is the benchmark's "
-                "default command (1000 warm-up and 1000 timed launches); its average covers all of them.\n\n")
+                "default command (1000 warm-up and 1000 timed steps); the timed-launch average covers the "
+                "kernel's launches in its timed steps, the figure comparable with that run's time per step.  "
+                "Counter passes run `--profile-steps` steps after their own warm-up; per-launch counter "
+                "figures are averages over those steps.\n\n")
         for k, c in cmds.items():
             f.write(f"- {k}: `{c}`\n")
     print(json.dumps(d))
@@ -690,7 +741,12 @@ def main():
     ap.add_argument("--profile-counters", default="",
                     help="extra counter passes for --profile: groups separated by ';', counters by ','")
     ap.add_argument("--profile-warmup", type=int, default=3, help="warm-up launches of the extra counter passes")
+    ap.add_argument("--profile-summarize", metavar="OUTDIR",
+                    help="only rewrite the summaries from the raw output an earlier --profile left in OUTDIR")
     args = ap.parse_args()
+    if args.profile_summarize:
+        summarize_profile(args.workload, args.profile_summarize)
+        return
     if args.profile:
         groups = [[c for c in g.split(",") if c] for g in args.profile_counters.split(";") if g.strip()]
         profile(args.workload, args.profile, args.profile_steps, groups, args.profile_warmup)
