@@ -1697,6 +1697,65 @@ __device__ __forceinline__ void quant_tile(const CodecArgs& a, const MapLDS& M, 
         if (FULL || blk0 + q / L::QPB < a.nb) store_code_word<FULL>(a.codes, L::elem(base, lane, q), n, w[q]);
 }
 
+// Quantize one tile with the binary-search encoder (maps without search tables): two
+// passes holding one quad at a time -- the block maxima first, then each quad is read
+// again and encoded -- so that this path, which only other maps take, does not raise
+// the register count of the kernel's table path.  The same arithmetic as quant_tile.
+template <int DT, int BS>
+__device__ __forceinline__ void quant_tile_search(const CodecArgs& a, const MapLDS& M, int64_t base, int lane) {
+    using L = Layout<BS>;
+    const int64_t n = a.n;
+    const int64_t blk0 = base / BS;
+    const bool full = a.vec && base + L::TE <= n;
+    auto quad = [&](int q, float (&v)[4]) {
+        const int64_t e = L::elem(base, lane, q);
+        if (full) {
+            load4<DT>(a.x, e, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = e + i < n ? load1<DT>(a.x, e + i) : 0.0f;
+        }
+    };
+    float m[L::BPT];
+#pragma unroll
+    for (int b = 0; b < L::BPT; ++b) {
+        float x = 0.0f;
+#pragma unroll 1
+        for (int qq = 0; qq < L::QPB; ++qq) {
+            float v[4];
+            quad(b * L::QPB + qq, v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x = fmaxf(x, fabsf(v[i]));
+        }
+        m[b] = x;
+    }
+    float u, ru, cu;
+    block_absmax_lanes<L::BPT>(m, u, ru, cu);
+    uint32_t wmask = 0;
+#pragma unroll
+    for (int b = 0; b < L::BPT; ++b) wmask |= (blk0 + b < a.nb) ? 1u << b : 0u;
+    store_absmax<L::BPT>(a.absmax, blk0, lane, u, wmask);
+#pragma unroll
+    for (int b = 0; b < L::BPT; ++b) {
+        if (!((wmask >> b) & 1u)) continue;                 // uniform
+        const float rq = block_value<L::BPT>(ru, b), cq = block_value<L::BPT>(cu, b);
+#pragma unroll 1
+        for (int qq = 0; qq < L::QPB; ++qq) {
+            const int q = b * L::QPB + qq;
+            float v[4];
+            quad(q, v);
+            uint32_t x = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x |= encode<false>(M, (v[i] * cq) * rq) << (8 * i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (full) store_code_word<true>(a.codes, L::elem(base, lane, q), n, x);
+            else store_code_word<false>(a.codes, L::elem(base, lane, q), n, x);
+        }
+    }
+}
+
 template <int DT, int BS, bool FAST>
 __device__ __forceinline__ void quant_tiles(const CodecArgs& a, const MapLDS& M) {
     constexpr int64_t TE = Layout<BS>::TE;
@@ -1705,13 +1764,14 @@ __device__ __forceinline__ void quant_tiles(const CodecArgs& a, const MapLDS& M)
     const int64_t ntiles = (a.n + TE - 1) / TE;
     for (int64_t t = wave_id(); t < ntiles; t += nwaves) {
         const int64_t base = t * TE;
-        if (a.vec && base + TE <= a.n) quant_tile<DT, BS, FAST, true>(a, M, base, lane);
-        else quant_tile<DT, BS, FAST, false>(a, M, base, lane);
+        if constexpr (!FAST) quant_tile_search<DT, BS>(a, M, base, lane);
+        else if (a.vec && base + TE <= a.n) quant_tile<DT, BS, true, true>(a, M, base, lane);
+        else quant_tile<DT, BS, true, false>(a, M, base, lane);
     }
 }
 
 template <int DT, int BS>
-__global__ __launch_bounds__(kThreads) void k_quantize(CodecArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BS == 256 ? 8 : 1))) void k_quantize(CodecArgs a) {
     __shared__ float Q[256], T[256];
     __shared__ __attribute__((aligned(16))) uint8_t B[search::kNB];
     __shared__ uint32_t vote[kWavesPerGroup];
