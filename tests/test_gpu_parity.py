@@ -335,6 +335,22 @@ def test_codec_custom_maps(dtype, bs):
                                                                                        bs, dtype))
 
 
+@pytest.mark.parametrize("bs", [256, 2048])
+def test_codec_custom_map_unaligned(bs):
+    """The binary-search encoder's element-wise path: input and codes one element off
+    their vector alignment, a ragged tail."""
+    n = 2 * bs + 301
+    print(f"\n[case] codec custom map unaligned B={bs} n={n}", flush=True)
+    x = W.normal_f32([906, bs], n + 1, 0.01)
+    qmap = _jittered_map(True, 43)
+    codes_ref, absmax_ref = oracle.quantize_blockwise(x[1:], "f32", qmap, bs)
+    qd = torch.from_numpy(qmap).cuda()
+    cbuf = torch.zeros(n + 1, dtype=torch.uint8, device="cuda")
+    codes, absmax = bitopt.quantize_blockwise(to_dev(x)[1:], qd, bs, codes=cbuf[1:])
+    np.testing.assert_array_equal(to_host(codes), codes_ref)
+    np.testing.assert_array_equal(to_host(absmax), absmax_ref)
+
+
 # ------------------------------------------------------------------ non-finite inputs
 # Reading (the pages are silent): a block's absmax ignores NaN values; a NaN normalized
 # value (a NaN state, or an infinite state in a block whose absmax is then infinite)
