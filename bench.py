@@ -753,7 +753,7 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the optimizer step is per-rank local (blocks are independent), "
-              "and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+              "and this library has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     dev = torch.device("cuda:0")

@@ -34,7 +34,7 @@ OPTS = {
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
-    bitopt.lib()          # a missing library is an error on a GPU machine, not a skip
+    bitopt.lib()          # a missing library is an error where a GPU is present, not a skip
 
 
 def _grad(seed, t, n, dtype, zero_frac=0.0, B=256):
