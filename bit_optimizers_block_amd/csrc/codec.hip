@@ -3,10 +3,16 @@
 
 namespace bitopt {
 
+// quantize runs a resident grid -- as many groups per CU as its occupancy allows, each
+// wave looping over tiles -- so that each group stages the map and its search tables
+// (about 10 KB) once rather than once per four tiles: 4096x4096 fp32 0.653 -> 0.673 of
+// HBM peak, bf16 0.505 -> 0.588 (one box).  dequantize stages 1 KB and keeps one tile per
+// wave (a resident grid measured slower).
 template <int DT, int BS>
 static hipError_t quant_one(const CodecArgs& a, hipStream_t s) {
     constexpr int64_t tile = Layout<BS>::TE;
-    hipLaunchKernelGGL((k_quantize<DT, BS>), tile_grid(a.n, tile), dim3(kThreads), 0, s, a);
+    static const int per_cu = resident_groups_per_cu(reinterpret_cast<const void*>(&k_quantize<DT, BS>));
+    hipLaunchKernelGGL((k_quantize<DT, BS>), tile_grid(a.n, tile, per_cu), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
